@@ -1,0 +1,145 @@
+/*
+ * rra.h -- C ABI of librra.so: variable-length (packed-sequence) attention
+ * forward pass and paged-KV grouped-query decode attention for AMD MI355X
+ * (gfx950).
+ *
+ * Conventions for every entry point
+ *   - Tensors are passed as plain device pointers; bf16 tensors as void*.
+ *     All tensors are dense, row-major, and must not alias one another.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns without synchronising.
+ *   - Arguments are validated on the host before any HIP call; a rejected
+ *     call launches nothing and returns a status below.  Launch failures
+ *     reported by the HIP runtime return RRA_ERR_HIP.  No C++ exception
+ *     crosses this boundary.
+ *   - The library keeps no device allocations of its own: the caller owns
+ *     every buffer (outputs and the decode workspace included).
+ *   - The contents of device-side index arrays (cu_seqlens, block tables,
+ *     context lengths) are preconditions, as stated per entry point; they are
+ *     not read on the host.
+ *
+ * Sources are cited by page title and section:
+ *   [PLAN]   "Varlen Flash Attention Implementation Plan" (rustytorch)
+ *   [DECODE] "spark_storage/attention_ref.rs"
+ */
+#ifndef RRA_H
+#define RRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define RRA_OK                 0
+#define RRA_ERR_INVALID_ARG    1  /* bad size, null pointer with work to do, bad scale, ... */
+#define RRA_ERR_UNSUPPORTED    2  /* valid but not implemented (e.g. head_dim not 64/128/256) */
+#define RRA_ERR_WORKSPACE      3  /* decode workspace missing or too small */
+#define RRA_ERR_HIP            4  /* the HIP runtime reported an error at launch */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *rra_status_string(int32_t status);
+
+/*
+ * Variable-length attention forward ([PLAN] Task 1, kernel signature and
+ * preconditions; Task 2, forward wrapper arguments).
+ *
+ * For every sequence b, head h and local query i of that sequence:
+ *   out[cu_q[b]+i, h, :] = softmax_j(softmax_scale * q_i . k_j  over visible j) . V
+ *   lse[cu_q[b]+i, h]    = log-sum-exp of the same scaled scores (natural log)
+ * with fp32 accumulation and bf16 rounding of the output.  Key j of sequence b
+ * (0 <= j < Lk_b) is visible to query i (0 <= i < Lq_b) when causal == 0, or
+ * when j <= i + Lk_b - Lq_b (bottom-right aligned causal mask; for Lq == Lk this
+ * is the usual "no key after the query" rule).  A query with no visible key
+ * gets out = 0 and lse = -inf.
+ *
+ *   q, out        bf16 [total_q, num_heads, head_dim]; element (t,h,d) at (t*H+h)*D+d
+ *   k, v          bf16 [total_k, num_heads, head_dim]
+ *   lse           fp32 [total_q, num_heads]; element (t,h) at t*H+h
+ *   cu_seqlens_q  int32 [batch+1] device array: 0 = cu[0] <= cu[1] <= ... ,
+ *   cu_seqlens_k  sequence b owns tokens [cu[b], cu[b+1]); cu[batch] = total
+ *   max_seqlen_q  >= every query length cu_q[b+1]-cu_q[b] (sizes the launch)
+ *   batch         number of sequences (0 = nothing to do, returns RRA_OK)
+ *   num_heads     > 0
+ *   head_dim      64, 128 or 256 (others: RRA_ERR_UNSUPPORTED)
+ *   softmax_scale finite and > 0
+ *   causal        0 or 1
+ * Rows of out/lse for tokens outside every query sequence are not written.
+ */
+int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                            int32_t max_seqlen_q, int32_t batch, int32_t num_heads,
+                            int32_t head_dim, float softmax_scale, int32_t causal, void *stream);
+
+/* Query rows per work item of rra_varlen_attn_fwd at this head_dim (0 if
+ * head_dim is unsupported).  Work items are (sequence, query tile, head). */
+int32_t rra_varlen_block_q(int32_t head_dim);
+
+/*
+ * Paged-KV grouped-query decode attention ([DECODE] AttnState, step_tile_ref,
+ * finalize_ref): one query token per sequence attends to the first
+ * context_lens[s] tokens of its paged K/V.
+ *
+ *   q, out        bf16 [num_seqs, num_q_heads, head_dim]
+ *   k_pool,v_pool bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_table   int32 [num_seqs, max_blocks_per_seq] device array; token t of
+ *                 sequence s is slot t % block_size of pool block
+ *                 block_table[s, t / block_size]; entries at or past
+ *                 ceil(context_lens[s] / block_size) are never read
+ *   context_lens  int32 [num_seqs] device array, 0 <= ctx <= max_blocks_per_seq*block_size
+ *   num_q_heads   multiple of num_kv_heads; q head qh reads kv head
+ *                 qh / (num_q_heads / num_kv_heads) (contiguous groups)
+ *   head_dim      64, 128 or 256
+ *   block_size    power of two in [1, 1024]
+ *   softmax_scale finite and > 0
+ *   workspace     device buffer of at least rra_paged_decode_workspace_bytes(...)
+ *                 bytes (fp32 partial softmax state of each split), owned by the
+ *                 caller; its contents on entry do not matter
+ * out = sum_t softmax_t(softmax_scale * q . K_t) V_t over t < context_lens[s],
+ * and out = 0 for a sequence with context length 0.  Two kernels run on
+ * `stream`: per-split partial state, then a combine that writes out.
+ */
+int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *block_table, const int32_t *context_lens, void *out,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              float softmax_scale, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Workspace bytes rra_paged_decode_attn needs for these sizes (0 if the sizes
+ * are invalid). */
+size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * Test hooks (integer work, checked bit-exactly against an independent
+ * definition).
+ *
+ * rra_debug_varlen_tile_map: runs the forward kernel's own work-item decoder
+ * for every launched work item and writes items_out[3*w..3*w+2] =
+ * (sequence, query tile, head) of item w, or (-1,-1,-1) for launched items
+ * beyond the last one.  *item_count receives the number of launched items
+ * (host value).  items_out must hold 3 * capacity int32; capacity must be at
+ * least the launched count, which is batch * ceil(max_seqlen_q / block_q) *
+ * num_heads.  block_q = rra_varlen_block_q(head_dim).  Synchronises `stream`.
+ */
+int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,
+                                  int32_t max_seqlen_q, int32_t head_dim, int32_t *items_out,
+                                  int64_t capacity, int64_t *item_count, void *stream);
+
+/*
+ * rra_debug_paged_gather: copies, with the decode kernel's own block-table
+ * address computation, every visible pool row into
+ * dense[s, t, kh, :] (bf16 [num_seqs, max_blocks_per_seq*block_size, num_kv_heads, head_dim])
+ * for t < context_lens[s]; other rows of dense are left untouched.
+ */
+int32_t rra_debug_paged_gather(const void *pool, const int32_t *block_table, const int32_t *context_lens,
+                               void *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t max_blocks_per_seq, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RRA_H */

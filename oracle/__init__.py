@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for variable-length attention and paged GQA decode.
+
+Test infrastructure only: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it; the GPU library never does.  See ``oracle.c`` for the
+definitions and the page sections they follow.
+"""
+from .oracle import (  # noqa: F401
+    build,
+    load,
+    varlen_attn,
+    varlen_attn_rows,
+    paged_decode,
+    paged_decode_recurrent,
+    paged_gather,
+    varlen_tile_map,
+    default_threads,
+)

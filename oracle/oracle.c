@@ -1,0 +1,442 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU reference for variable-length (packed)
+ * attention and for paged-KV GQA decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links or calls it, and it shares no code, header or table with the GPU
+ * kernels.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [PLAN]   "Varlen Flash Attention Implementation Plan" (rustytorch,
+ *            docs/superpowers/plans/2026-06-27-varlen-flash-attention.md)
+ *            -- Task 1 (CUDA kernel source) and Task 2 (CPU simulation
+ *            varlen_attention_cpu, its tests).
+ *   [DECODE] "spark_storage/attention_ref.rs" -- AttnState, step_tile_ref,
+ *            finalize_ref.
+ *
+ * Arithmetic: every bf16 input is widened exactly to double; all sums,
+ * exponentials and logarithms are double (libm).  Nothing is blocked, fused
+ * or reordered beyond what the definitions below state.
+ *
+ * Readings of the pages that this file fixes (each one also listed in the
+ * design notes):
+ *   - causal masking is bottom-right aligned: query i of a sequence with
+ *     Lq queries and Lk keys sees key j iff j <= i + Lk - Lq (for Lq == Lk
+ *     this is the PLAN kernel's "k_pos > q_pos is masked" rule);
+ *   - a query with no visible key gets out = 0 and lse = -inf (the PLAN
+ *     kernel writes 0 for out when the denominator is 0; -inf is the exact
+ *     log-sum-exp of an empty set);
+ *   - lse is natural-log, in the scaled-score domain: lse = m + ln(l)
+ *     ([PLAN] Task 1, "Write output and LSE");
+ *   - decode only counts the first context_lens[s] tokens of a sequence; a
+ *     partially filled last block is cut at the context length.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* bf16 is the top half of an IEEE binary32; widening is exact. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Simple static work split over POSIX threads.                             */
+/* ------------------------------------------------------------------------ */
+typedef void (*unit_fn)(void *ctx, int64_t unit, double *scratch);
+
+typedef struct {
+    unit_fn fn;
+    void *ctx;
+    int64_t n_units;
+    int64_t first, step;
+    size_t scratch_len;
+} worker_args;
+
+static void *worker_main(void *p)
+{
+    worker_args *a = (worker_args *)p;
+    double *scratch = (double *)malloc((a->scratch_len ? a->scratch_len : 1) * sizeof(double));
+    if (!scratch) return (void *)1;
+    for (int64_t u = a->first; u < a->n_units; u += a->step) a->fn(a->ctx, u, scratch);
+    free(scratch);
+    return NULL;
+}
+
+static int run_units(unit_fn fn, void *ctx, int64_t n_units, size_t scratch_len, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    if (n_units < nthreads) nthreads = (int)(n_units > 0 ? n_units : 1);
+    pthread_t tid[512];
+    worker_args args[512];
+    int rc = 0;
+    for (int t = 0; t < nthreads; t++) {
+        args[t].fn = fn; args[t].ctx = ctx; args[t].n_units = n_units;
+        args[t].first = t; args[t].step = nthreads; args[t].scratch_len = scratch_len;
+    }
+    if (nthreads == 1) return worker_main(&args[0]) == NULL ? 0 : -1;
+    int started = 0;
+    for (int t = 0; t < nthreads; t++) {
+        if (pthread_create(&tid[t], NULL, worker_main, &args[t]) != 0) { rc = -1; break; }
+        started++;
+    }
+    for (int t = 0; t < started; t++) {
+        void *ret = NULL;
+        pthread_join(tid[t], &ret);
+        if (ret != NULL) rc = -1;
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Variable-length attention forward.                                       */
+/*                                                                          */
+/* Layout ([PLAN] Task 1 preconditions; Task 2 "Layout"): q, out are        */
+/* [total_q, H, D], k, v are [total_k, H, D], element (t, h, d) at          */
+/* (t*H + h)*D + d.  lse is [total_q, H].  Sequence b owns the half-open    */
+/* token ranges [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]).              */
+/*                                                                          */
+/* For query i of sequence b and head h, with A(i) the visible keys:        */
+/*   s_j = scale * sum_d q[i,d] k[j,d]                 (j in A(i))          */
+/*   M   = max_j s_j,   Z = sum_j exp(s_j - M)                              */
+/*   out = sum_j exp(s_j - M) v_j / Z,   lse = M + ln Z                     */
+/* computed in the order of the PLAN's CPU simulation: scores for the row,  */
+/* then the row max, then the exponential sum, then the weighted V sum.     */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const uint16_t *q, *k, *v;
+    const int32_t *cu_q, *cu_k;
+    int32_t batch, H, D;
+    double scale;
+    int32_t causal;
+    double *out, *lse;
+    /* sampled-row mode */
+    const int32_t *rows; /* pairs (token, head) */
+} varlen_ctx;
+
+/* Is key j visible to query i?  Bottom-right causal alignment. */
+static int key_visible(int64_t i, int64_t j, int64_t Lq, int64_t Lk, int causal)
+{
+    if (j < 0 || j >= Lk) return 0;
+    if (!causal) return 1;
+    return j <= i + Lk - Lq;
+}
+
+/* One output row: sequence b, local query i, head h.  scratch holds Lk doubles. */
+static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
+                       double *scratch, double *out_row, double *lse_out)
+{
+    const int64_t H = c->H, D = c->D;
+    const int64_t q0 = c->cu_q[b], k0 = c->cu_k[b];
+    const int64_t Lq = (int64_t)c->cu_q[b + 1] - q0;
+    const int64_t Lk = (int64_t)c->cu_k[b + 1] - k0;
+    const uint16_t *qrow = c->q + ((q0 + i) * H + h) * D;
+
+    /* scores of the visible keys, and their maximum */
+    double M = -INFINITY;
+    int64_t n_visible = 0;
+    for (int64_t j = 0; j < Lk; j++) {
+        if (!key_visible(i, j, Lq, Lk, c->causal)) { scratch[j] = -INFINITY; continue; }
+        const uint16_t *krow = c->k + ((k0 + j) * H + h) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(krow[d]);
+        scratch[j] = c->scale * dot;
+        if (scratch[j] > M) M = scratch[j];
+        n_visible++;
+    }
+    if (n_visible == 0) {
+        for (int64_t d = 0; d < D; d++) out_row[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+    /* normaliser */
+    double Z = 0.0;
+    for (int64_t j = 0; j < Lk; j++)
+        if (key_visible(i, j, Lq, Lk, c->causal)) Z += exp(scratch[j] - M);
+    /* weighted sum of values */
+    for (int64_t d = 0; d < D; d++) out_row[d] = 0.0;
+    for (int64_t j = 0; j < Lk; j++) {
+        if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
+        const double w = exp(scratch[j] - M) / Z;
+        const uint16_t *vrow = c->v + ((k0 + j) * H + h) * D;
+        for (int64_t d = 0; d < D; d++) out_row[d] += w * bf16_value(vrow[d]);
+    }
+    *lse_out = M + log(Z);
+}
+
+/* unit = b*H + h : every query row of one (sequence, head) */
+static void varlen_unit(void *p, int64_t unit, double *scratch)
+{
+    const varlen_ctx *c = (const varlen_ctx *)p;
+    const int32_t b = (int32_t)(unit / c->H), h = (int32_t)(unit % c->H);
+    const int64_t q0 = c->cu_q[b];
+    const int64_t Lq = (int64_t)c->cu_q[b + 1] - q0;
+    for (int64_t i = 0; i < Lq; i++) {
+        const int64_t t = q0 + i;
+        varlen_row(c, b, i, h, scratch, c->out + (t * c->H + h) * c->D, c->lse + t * c->H + h);
+    }
+}
+
+static int64_t max_len(const int32_t *cu, int32_t batch)
+{
+    int64_t m = 0;
+    for (int32_t b = 0; b < batch; b++) {
+        const int64_t L = (int64_t)cu[b + 1] - cu[b];
+        if (L > m) m = L;
+    }
+    return m;
+}
+
+/* Returns 0 on success, -1 on bad arguments or allocation failure. */
+int oracle_varlen_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
+                       int32_t num_heads, int32_t head_dim, double scale, int32_t causal,
+                       double *out, double *lse, int32_t nthreads)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0) return -1;
+    for (int32_t b = 0; b < batch; b++)
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
+    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, NULL};
+    return run_units(varlen_unit, &c, (int64_t)batch * num_heads, (size_t)max_len(cu_k, batch), nthreads);
+}
+
+/* Sampled rows: rows[2r] = packed query token, rows[2r+1] = head.  Writes
+ * out[r*D .. r*D+D) and lse[r].  The owning sequence of a token is the b
+ * with cu_q[b] <= token < cu_q[b+1]. */
+static void varlen_sample_unit(void *p, int64_t r, double *scratch)
+{
+    const varlen_ctx *c = (const varlen_ctx *)p;
+    const int32_t t = c->rows[2 * r], h = c->rows[2 * r + 1];
+    int32_t b = 0;
+    while (!(c->cu_q[b] <= t && t < c->cu_q[b + 1])) b++;
+    varlen_row(c, b, (int64_t)t - c->cu_q[b], h, scratch, c->out + r * c->D, c->lse + r);
+}
+
+int oracle_varlen_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
+                            int32_t num_heads, int32_t head_dim, double scale, int32_t causal,
+                            const int32_t *rows, int64_t n_rows,
+                            double *out, double *lse, int32_t nthreads)
+{
+    if (batch <= 0 || num_heads <= 0 || head_dim <= 0) return -1;
+    for (int64_t r = 0; r < n_rows; r++) {
+        if (rows[2 * r] < cu_q[0] || rows[2 * r] >= cu_q[batch]) return -1;
+        if (rows[2 * r + 1] < 0 || rows[2 * r + 1] >= num_heads) return -1;
+    }
+    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, rows};
+    return run_units(varlen_sample_unit, &c, n_rows, (size_t)max_len(cu_k, batch), nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Paged-KV GQA decode.                                                     */
+/*                                                                          */
+/* [DECODE] layout: q, out [S, Hq, D]; k_pool, v_pool [NB, BS, Hkv, D];     */
+/* token t of sequence s lives in physical block block_table[s, t / BS] at  */
+/* slot t % BS; the q head qh reads kv head qh / (Hq / Hkv).                */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const uint16_t *q, *k_pool, *v_pool;
+    const int32_t *block_table, *context_lens;
+    int32_t S, Hq, Hkv, D, BS, max_blocks;
+    double scale;
+    int32_t tile_capacity; /* recurrent route only */
+    double *out;
+} decode_ctx;
+
+static const uint16_t *pool_row(const decode_ctx *c, const uint16_t *pool, int32_t s, int64_t t, int32_t kh)
+{
+    const int64_t blk = c->block_table[(int64_t)s * c->max_blocks + t / c->BS];
+    const int64_t slot = t % c->BS;
+    return pool + ((blk * c->BS + slot) * c->Hkv + kh) * c->D;
+}
+
+/* Direct definition: out = softmax_t(scale * q.K_t) . V_t over t < ctx. */
+static void decode_direct_unit(void *p, int64_t unit, double *scratch)
+{
+    const decode_ctx *c = (const decode_ctx *)p;
+    const int32_t s = (int32_t)(unit / c->Hq), qh = (int32_t)(unit % c->Hq);
+    const int32_t kh = qh / (c->Hq / c->Hkv);
+    const int64_t ctx = c->context_lens[s], D = c->D;
+    const uint16_t *qrow = c->q + ((int64_t)s * c->Hq + qh) * D;
+    double *o = c->out + ((int64_t)s * c->Hq + qh) * D;
+    for (int64_t d = 0; d < D; d++) o[d] = 0.0;
+    if (ctx <= 0) return;
+    double M = -INFINITY;
+    for (int64_t t = 0; t < ctx; t++) {
+        const uint16_t *kr = pool_row(c, c->k_pool, s, t, kh);
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(kr[d]);
+        scratch[t] = c->scale * dot;
+        if (scratch[t] > M) M = scratch[t];
+    }
+    double Z = 0.0;
+    for (int64_t t = 0; t < ctx; t++) Z += exp(scratch[t] - M);
+    for (int64_t t = 0; t < ctx; t++) {
+        const double w = exp(scratch[t] - M) / Z;
+        const uint16_t *vr = pool_row(c, c->v_pool, s, t, kh);
+        for (int64_t d = 0; d < D; d++) o[d] += w * bf16_value(vr[d]);
+    }
+}
+
+/* The decode page's route: running state (m, l, o) starting at (-inf, 0, 0),
+ * one token at a time in block-table order:
+ *   m' = max(m, x);  l = l*exp(m - m') + exp(x - m');  o = o*exp(m - m') + exp(x - m')*v;  m = m'
+ * with the state stored and reloaded between tiles of tile_capacity blocks
+ * (AttnState carried across step_tile_ref calls), then finalize:
+ * out = o / l if l > 0 else 0 (finalize_ref). */
+static void decode_recurrent_unit(void *p, int64_t unit, double *scratch)
+{
+    (void)scratch;
+    const decode_ctx *c = (const decode_ctx *)p;
+    const int32_t s = (int32_t)(unit / c->Hq), qh = (int32_t)(unit % c->Hq);
+    const int32_t kh = qh / (c->Hq / c->Hkv);
+    const int64_t ctx = c->context_lens[s], D = c->D;
+    const uint16_t *qrow = c->q + ((int64_t)s * c->Hq + qh) * D;
+    double *o_out = c->out + ((int64_t)s * c->Hq + qh) * D;
+
+    /* carried state, as kept between tile calls */
+    double st_m = -INFINITY, st_l = 0.0;
+    double *st_o = scratch; /* D doubles */
+    for (int64_t d = 0; d < D; d++) st_o[d] = 0.0;
+
+    const int64_t n_blocks = (ctx + c->BS - 1) / c->BS;
+    for (int64_t tile0 = 0; tile0 < n_blocks; tile0 += c->tile_capacity) {
+        double m = st_m, l = st_l; /* load state */
+        double *o = st_o;
+        const int64_t tile1 = tile0 + c->tile_capacity < n_blocks ? tile0 + c->tile_capacity : n_blocks;
+        for (int64_t blk = tile0; blk < tile1; blk++) {
+            for (int64_t slot = 0; slot < c->BS; slot++) {
+                const int64_t t = blk * c->BS + slot;
+                if (t >= ctx) break;
+                const uint16_t *kr = pool_row(c, c->k_pool, s, t, kh);
+                const uint16_t *vr = pool_row(c, c->v_pool, s, t, kh);
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(kr[d]);
+                const double x = c->scale * dot;
+                const double m_new = x > m ? x : m;
+                const double scale_old = exp(m - m_new);
+                const double scale_new = exp(x - m_new);
+                l = l * scale_old + scale_new;
+                for (int64_t d = 0; d < D; d++) o[d] = o[d] * scale_old + scale_new * bf16_value(vr[d]);
+                m = m_new;
+            }
+        }
+        st_m = m; st_l = l; /* store state */
+    }
+    const double inv_l = st_l > 0.0 ? 1.0 / st_l : 0.0;
+    for (int64_t d = 0; d < D; d++) o_out[d] = st_o[d] * inv_l;
+}
+
+static int decode_check(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                        int32_t max_blocks, const int32_t *context_lens)
+{
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || max_blocks < 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    for (int32_t s = 0; s < S; s++)
+        if (context_lens[s] < 0 || context_lens[s] > (int64_t)max_blocks * BS) return -1;
+    return 0;
+}
+
+static int64_t max_ctx(const int32_t *context_lens, int32_t S)
+{
+    int64_t m = 1;
+    for (int32_t s = 0; s < S; s++) if (context_lens[s] > m) m = context_lens[s];
+    return m;
+}
+
+int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                        const int32_t *block_table, const int32_t *context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        double scale, double *out, int32_t nthreads)
+{
+    if (decode_check(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, context_lens))
+        return -1;
+    decode_ctx c = {q, k_pool, v_pool, block_table, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                    head_dim, block_size, max_blocks_per_seq, scale, 0, out};
+    return run_units(decode_direct_unit, &c, (int64_t)num_seqs * num_q_heads,
+                     (size_t)max_ctx(context_lens, num_seqs), nthreads);
+}
+
+int oracle_paged_decode_recurrent(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                  const int32_t *block_table, const int32_t *context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                  double scale, int32_t tile_capacity, double *out, int32_t nthreads)
+{
+    if (decode_check(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, context_lens))
+        return -1;
+    if (tile_capacity <= 0) return -1;
+    decode_ctx c = {q, k_pool, v_pool, block_table, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                    head_dim, block_size, max_blocks_per_seq, scale, tile_capacity, out};
+    return run_units(decode_recurrent_unit, &c, (int64_t)num_seqs * num_q_heads, (size_t)head_dim, nthreads);
+}
+
+/* Gather of the visible pool rows of every sequence into a dense buffer
+ * [S, max_blocks*BS, Hkv, D] (bf16 bit copies); rows t >= ctx are left as
+ * the caller filled them.  This is the block-table indexing alone. */
+int oracle_paged_gather(const uint16_t *pool, const int32_t *block_table, const int32_t *context_lens,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, uint16_t *dense)
+{
+    if (decode_check(num_seqs, num_kv_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, context_lens))
+        return -1;
+    decode_ctx c = {NULL, pool, NULL, block_table, context_lens, num_seqs, num_kv_heads, num_kv_heads,
+                    head_dim, block_size, max_blocks_per_seq, 1.0, 0, NULL};
+    const int64_t T = (int64_t)max_blocks_per_seq * block_size;
+    for (int32_t s = 0; s < num_seqs; s++)
+        for (int64_t t = 0; t < context_lens[s]; t++)
+            for (int32_t kh = 0; kh < num_kv_heads; kh++)
+                memcpy(dense + (((int64_t)s * T + t) * num_kv_heads + kh) * head_dim,
+                       pool_row(&c, pool, s, t, kh), (size_t)head_dim * sizeof(uint16_t));
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Work list of the tiled forward pass (integer work).                      */
+/*                                                                          */
+/* Sequence b is cut into n_b = ceil(Lq_b / block_q) query tiles.  Tiles are */
+/* listed level by level: level r holds tile index qt = r of every sequence */
+/* with n_b > r, in ascending b; levels run from the highest r down to 0.   */
+/* Under causal masking with Lq == Lk a tile at level r sees r+1 key tiles, */
+/* so this lists the most expensive tiles first.  Each tile expands into    */
+/* num_heads items, head innermost: item = tile_position * H + h.           */
+/* Output: items[3*w .. 3*w+2] = (b, qt, h).  Returns the item count, or    */
+/* -1 if capacity is too small or arguments are bad.                        */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_heads, int32_t block_q,
+                               int32_t *items, int64_t capacity)
+{
+    if (batch < 0 || num_heads <= 0 || block_q <= 0) return -1;
+    int64_t max_tiles = 0;
+    for (int32_t b = 0; b < batch; b++) {
+        const int64_t L = (int64_t)cu_q[b + 1] - cu_q[b];
+        if (L < 0) return -1;
+        const int64_t n = (L + block_q - 1) / block_q;
+        if (n > max_tiles) max_tiles = n;
+    }
+    int64_t w = 0;
+    for (int64_t r = max_tiles - 1; r >= 0; r--) {
+        for (int32_t b = 0; b < batch; b++) {
+            const int64_t L = (int64_t)cu_q[b + 1] - cu_q[b];
+            const int64_t n = (L + block_q - 1) / block_q;
+            if (n <= r) continue;
+            for (int32_t h = 0; h < num_heads; h++) {
+                if (w >= capacity) return -1;
+                items[3 * w + 0] = b;
+                items[3 * w + 1] = (int32_t)r;
+                items[3 * w + 2] = h;
+                w++;
+            }
+        }
+    }
+    return w;
+}

@@ -1,0 +1,174 @@
+"""ctypes front end of ``liboracle.so`` (the fp64 CPU oracle).
+
+Test infrastructure only.  Inputs are bf16 bit patterns (``numpy.uint16``)
+exactly as they are handed to the GPU; outputs are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (plain C99, -O2, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", *extra_flags,
+           "-o", out, src, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _bind(lib):
+    u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+    i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_varlen_attn.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, f64, i32, f64p, f64p, i32]
+    lib.oracle_varlen_attn.restype = ctypes.c_int
+    lib.oracle_varlen_attn_rows.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, f64, i32,
+                                            i32p, i64, f64p, f64p, i32]
+    lib.oracle_varlen_attn_rows.restype = ctypes.c_int
+    lib.oracle_paged_decode.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32, f64, f64p, i32]
+    lib.oracle_paged_decode.restype = ctypes.c_int
+    lib.oracle_paged_decode_recurrent.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32,
+                                                  f64, i32, f64p, i32]
+    lib.oracle_paged_decode_recurrent.restype = ctypes.c_int
+    lib.oracle_paged_gather.argtypes = [u16p, i32p, i32p, i32, i32, i32, i32, i32, u16p]
+    lib.oracle_paged_gather.restype = ctypes.c_int
+    lib.oracle_varlen_tile_map.argtypes = [i32p, i32, i32, i32, i32p, i64]
+    lib.oracle_varlen_tile_map.restype = ctypes.c_int64
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library.  ``path`` selects
+    another build of it, e.g. a deliberately broken copy in a test."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def varlen_attn(q, k, v, cu_q, cu_k, scale, causal, nthreads=None, lib=None):
+    """Full oracle: q [Tq,H,D], k/v [Tk,H,D] uint16 bf16 bits; returns
+    (out [Tq,H,D] float64, lse [Tq,H] float64).  Rows of tokens outside every
+    sequence stay NaN."""
+    lib = lib or load()
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    Tq, H, D = q.shape
+    out = np.full((Tq, H, D), np.nan)
+    lse = np.full((Tq, H), np.nan)
+    rc = lib.oracle_varlen_attn(q, k, v, cu_q, cu_k, len(cu_q) - 1, H, D, float(scale), int(bool(causal)),
+                                out, lse, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_varlen_attn rejected its arguments")
+    return out, lse
+
+
+def varlen_attn_rows(q, k, v, cu_q, cu_k, scale, causal, rows, nthreads=None, lib=None):
+    """Oracle for selected rows only; ``rows`` is an int array [n, 2] of
+    (packed query token, head).  Returns (out [n, D], lse [n])."""
+    lib = lib or load()
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _c(rows, np.int32).reshape(-1, 2)
+    D = q.shape[2]
+    out = np.full((rows.shape[0], D), np.nan)
+    lse = np.full((rows.shape[0],), np.nan)
+    rc = lib.oracle_varlen_attn_rows(q, k, v, cu_q, cu_k, len(cu_q) - 1, q.shape[1], D, float(scale),
+                                     int(bool(causal)), rows, rows.shape[0], out, lse,
+                                     nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_varlen_attn_rows rejected its arguments")
+    return out, lse
+
+
+def _decode_args(q, k_pool, v_pool, block_table, context_lens):
+    q = _c(q, np.uint16)
+    k_pool, v_pool = _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    block_table, context_lens = _c(block_table, np.int32), _c(context_lens, np.int32)
+    S, Hq, D = q.shape
+    _, BS, Hkv, _ = k_pool.shape
+    return q, k_pool, v_pool, block_table, context_lens, S, Hq, Hkv, D, BS, block_table.shape[1]
+
+
+def paged_decode(q, k_pool, v_pool, block_table, context_lens, scale, nthreads=None, lib=None):
+    """Direct definition.  q [S,Hq,D]; pools [NB,BS,Hkv,D]; block_table
+    [S, max_blocks] int32; context_lens [S] int32.  Returns out [S,Hq,D] f64."""
+    lib = lib or load()
+    q, k_pool, v_pool, bt, cl, S, Hq, Hkv, D, BS, MB = _decode_args(q, k_pool, v_pool, block_table, context_lens)
+    out = np.full((S, Hq, D), np.nan)
+    rc = lib.oracle_paged_decode(q, k_pool, v_pool, bt, cl, S, Hq, Hkv, D, BS, MB, float(scale), out,
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_paged_decode rejected its arguments")
+    return out
+
+
+def paged_decode_recurrent(q, k_pool, v_pool, block_table, context_lens, scale, tile_capacity=1,
+                           nthreads=None, lib=None):
+    """The decode page's per-token (m, l, o) recurrence with the state carried
+    across tiles of ``tile_capacity`` blocks, then the l > 0 guarded finalize."""
+    lib = lib or load()
+    q, k_pool, v_pool, bt, cl, S, Hq, Hkv, D, BS, MB = _decode_args(q, k_pool, v_pool, block_table, context_lens)
+    out = np.full((S, Hq, D), np.nan)
+    rc = lib.oracle_paged_decode_recurrent(q, k_pool, v_pool, bt, cl, S, Hq, Hkv, D, BS, MB, float(scale),
+                                           int(tile_capacity), out, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_paged_decode_recurrent rejected its arguments")
+    return out
+
+
+def paged_gather(pool, block_table, context_lens, fill=0xFFFF, lib=None):
+    """Dense [S, max_blocks*BS, Hkv, D] copy of each sequence's visible pool
+    rows (bf16 bits); rows past the context length hold ``fill``."""
+    lib = lib or load()
+    pool = _c(pool, np.uint16)
+    bt, cl = _c(block_table, np.int32), _c(context_lens, np.int32)
+    _, BS, Hkv, D = pool.shape
+    S, MB = bt.shape
+    dense = np.full((S, MB * BS, Hkv, D), fill, dtype=np.uint16)
+    rc = lib.oracle_paged_gather(pool, bt, cl, S, Hkv, D, BS, MB, dense)
+    if rc != 0:
+        raise ValueError("oracle_paged_gather rejected its arguments")
+    return dense
+
+
+def varlen_tile_map(cu_q, num_heads, block_q, lib=None):
+    """Canonical work list of the tiled forward pass: int32 [n_items, 3] of
+    (sequence, query tile, head), most expensive tile level first."""
+    lib = lib or load()
+    cu_q = _c(cu_q, np.int32)
+    B = len(cu_q) - 1
+    cap = 0
+    for b in range(B):
+        cap += -(-(int(cu_q[b + 1]) - int(cu_q[b])) // block_q)
+    cap = max(cap * num_heads, 1)
+    items = np.zeros((cap, 3), dtype=np.int32)
+    n = lib.oracle_varlen_tile_map(cu_q, B, num_heads, block_q, items, cap)
+    if n < 0:
+        raise ValueError("oracle_varlen_tile_map rejected its arguments")
+    return items[:n]

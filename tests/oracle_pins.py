@@ -1,0 +1,367 @@
+"""Checks that pin the CPU oracle to facts fixed by the pages and by
+mathematics, independently of the oracle's own code.
+
+Every ``pin_*`` function takes a loaded oracle library handle (the real one,
+or a deliberately broken copy in the mutation test) and raises AssertionError
+when the oracle disagrees.  Sources: "Varlen Flash Attention Implementation
+Plan" (Task 1 kernel, Task 2 CPU simulation and tests) and
+"spark_storage/attention_ref.rs" (step_tile_ref, finalize_ref).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle as O
+from golden_cases import check as golden_check
+from golden_cases import golden_files
+from golden_cases import load as golden_load
+from variable_length_flashattention_amd.inputs import (bf16_bits, bf16_to_f32, cu_from_lengths, decode_case,
+                                                       varlen_case)
+
+
+# --- an independent brute force ------------------------------------------------
+
+def brute_force_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    """softmax over the whole packed [Tq x Tk] score matrix with a block
+    diagonal (same-sequence) mask and the bottom-right causal rule, summed with
+    math.fsum.  Written against the definition, not the oracle's loops."""
+    qf, kf, vf = (bf16_to_f32(x).astype(np.float64) for x in (q, k, v))
+    Tq, H, D = qf.shape
+    Tk = kf.shape[0]
+    B = len(cu_q) - 1
+    seq_q = np.full(Tq, -1)
+    seq_k = np.full(Tk, -1)
+    for b in range(B):
+        seq_q[cu_q[b]:cu_q[b + 1]] = b
+        seq_k[cu_k[b]:cu_k[b + 1]] = b
+    out = np.full((Tq, H, D), np.nan)
+    lse = np.full((Tq, H), np.nan)
+    for tq in range(Tq):
+        b = seq_q[tq]
+        if b < 0:
+            continue
+        i = tq - cu_q[b]
+        Lq, Lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for h in range(H):
+            logits = []
+            for tk in range(Tk):
+                if seq_k[tk] != b:
+                    continue
+                j = tk - cu_k[b]
+                if causal and j > i + Lk - Lq:
+                    continue
+                logits.append((scale * math.fsum(qf[tq, h, d] * kf[tk, h, d] for d in range(D)), tk))
+            if not logits:
+                out[tq, h] = 0.0
+                lse[tq, h] = -math.inf
+                continue
+            M = max(s for s, _ in logits)
+            w = [(math.exp(s - M), tk) for s, tk in logits]
+            Z = math.fsum(x for x, _ in w)
+            for d in range(D):
+                out[tq, h, d] = math.fsum(x * vf[tk, h, d] for x, tk in w) / Z
+            lse[tq, h] = M + math.log(Z)
+    return out, lse
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    with np.errstate(invalid="ignore"):
+        same_special = (np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))) | (np.isnan(a) & np.isnan(b))
+        ok = same_special | (np.abs(a - b) <= tol * (1.0 + np.abs(b)))
+    assert np.all(ok), f"{what}: max diff {np.nanmax(np.where(ok, 0, np.abs(a - b)))}"
+
+
+def _random_case(rng, B, H, D, max_len, allow_short_k=True):
+    lq = rng.integers(0, max_len + 1, size=B)
+    if allow_short_k:
+        lk = rng.integers(0, max_len + 1, size=B)
+    else:
+        lk = lq + rng.integers(0, 4, size=B)
+    return varlen_case("rand", lq, lk, H, D, int(rng.integers(1 << 30)), False, rng=rng)
+
+
+# --- prefill pins -----------------------------------------------------------------
+
+def pin_bruteforce_tiny(lib):
+    """Oracle == brute force on tiny random packs (empty sequences, Lk < Lq,
+    Lk > Lq, fully masked rows), both causal modes, within 1e-12."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    for trial in range(10):
+        c = _random_case(rng, B=int(rng.integers(1, 5)), H=int(rng.integers(1, 3)), D=int(rng.choice([4, 8, 16])),
+                         max_len=9)
+        for causal in (False, True):
+            o1, l1 = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+            o2, l2 = brute_force_varlen(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+            _close(o1, o2, 1e-12, f"out trial {trial} causal {causal}")
+            _close(l1, l2, 1e-12, f"lse trial {trial} causal {causal}")
+
+
+def pin_golden_plan_examples(lib):
+    """Worked examples of the plan page's CPU tests (tests/golden/plan_*.json)."""
+    def run(q, k, v, cu, scale, causal):
+        return O.varlen_attn(q, k, v, cu, cu, scale, causal, lib=lib)
+    files = golden_files("plan_")
+    assert len(files) == 6
+    for f in files:
+        golden_check(golden_load(f), run)
+
+
+def pin_constant_values(lib):
+    """V == c everywhere gives out == c on every row that sees a key."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    c = varlen_case("c", [5, 9, 1], [7, 9, 3], 2, 8, 3, False, rng=rng)
+    v = bf16_bits(np.full(c.v.shape, -1.75, np.float32))
+    for causal in (False, True):
+        out, lse = O.varlen_attn(c.q, c.k, v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+        _close(out, np.full(out.shape, -1.75), 1e-13, f"V==c causal {causal}")
+
+
+def pin_single_key(lib):
+    """One visible key j gives out == v_j and lse == scale * q.k_j."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    c = varlen_case("c", [3, 4], [1, 1], 2, 8, 4, False, rng=rng)
+    out, lse = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, False, lib=lib)
+    qf, kf, vf = (bf16_to_f32(x).astype(np.float64) for x in (c.q, c.k, c.v))
+    for b in range(2):
+        for t in range(c.cu_q[b], c.cu_q[b + 1]):
+            for h in range(2):
+                kt = c.cu_k[b]
+                _close(out[t, h], vf[kt, h], 1e-14, "single key out")
+                _close(lse[t, h], c.scale * float(np.dot(qf[t, h], kf[kt, h])), 1e-13, "single key lse")
+
+
+def pin_zero_query_uniform(lib):
+    """q == 0 gives uniform weights: out = mean of the visible v rows and
+    lse = ln(#visible).  With Lk > Lq the causal count is i + Lk - Lq + 1
+    (bottom-right); with Lk < Lq rows i < Lq - Lk see nothing (out 0, lse -inf)."""
+    rng = np.random.Generator(np.random.PCG64(14))
+    c = varlen_case("c", [4, 6], [7, 3], 1, 4, 5, False, rng=rng)
+    q0 = np.zeros_like(c.q)
+    vf = bf16_to_f32(c.v).astype(np.float64)
+    for causal in (False, True):
+        out, lse = O.varlen_attn(q0, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+        for b in range(2):
+            Lq, Lk = c.cu_q[b + 1] - c.cu_q[b], c.cu_k[b + 1] - c.cu_k[b]
+            for i in range(Lq):
+                n = Lk if not causal else max(0, min(Lk, i + Lk - Lq + 1))
+                t = c.cu_q[b] + i
+                if n == 0:
+                    assert np.all(out[t] == 0.0) and np.all(lse[t] == -np.inf), (b, i)
+                    continue
+                keys = slice(c.cu_k[b], c.cu_k[b] + n)
+                _close(out[t, 0], vf[keys, 0].mean(axis=0), 1e-14, f"uniform out b{b} i{i}")
+                _close(lse[t, 0], math.log(n), 1e-14, f"uniform lse b{b} i{i}")
+
+
+def pin_packed_equals_per_sequence(lib):
+    """Varlen output equals the output of each sequence run on its own."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    c = varlen_case("c", [5, 0, 12, 3], [5, 2, 12, 8], 2, 16, 6, False, rng=rng)
+    for causal in (False, True):
+        out, lse = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+        for b in range(c.batch):
+            qs, qe, ks, ke = c.cu_q[b], c.cu_q[b + 1], c.cu_k[b], c.cu_k[b + 1]
+            if qe == qs:
+                continue
+            cu1 = np.array([0, qe - qs], np.int32)
+            cuk1 = np.array([0, ke - ks], np.int32)
+            o1, l1 = O.varlen_attn(c.q[qs:qe], c.k[ks:ke], c.v[ks:ke], cu1, cuk1, c.scale, causal, lib=lib)
+            assert np.array_equal(o1, out[qs:qe]) and np.array_equal(l1, lse[qs:qe]), (b, causal)
+
+
+def pin_key_permutation(lib):
+    """Without a causal mask the result does not depend on key order within a sequence."""
+    rng = np.random.Generator(np.random.PCG64(16))
+    c = varlen_case("c", [6, 9], [10, 4], 2, 8, 7, False, rng=rng)
+    out, lse = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, False, lib=lib)
+    perm = np.arange(c.k.shape[0])
+    for b in range(c.batch):
+        perm[c.cu_k[b]:c.cu_k[b + 1]] = rng.permutation(np.arange(c.cu_k[b], c.cu_k[b + 1]))
+    o2, l2 = O.varlen_attn(c.q, c.k[perm], c.v[perm], c.cu_q, c.cu_k, c.scale, False, lib=lib)
+    _close(o2, out, 1e-13, "key permutation out")
+    _close(l2, lse, 1e-13, "key permutation lse")
+
+
+def pin_sequence_isolation_and_order(lib):
+    """Changing another sequence leaves a sequence's rows bit-identical;
+    reversing the sequence order reverses the rows."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    c = varlen_case("c", [4, 7, 3], [4, 9, 3], 2, 8, 8, True, rng=rng)
+    out, lse = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True, lib=lib)
+    k2, v2 = c.k.copy(), c.v.copy()
+    k2[c.cu_k[0]:c.cu_k[1]] = bf16_bits(rng.standard_normal(k2[c.cu_k[0]:c.cu_k[1]].shape).astype(np.float32))
+    v2[c.cu_k[2]:c.cu_k[3]] = bf16_bits(rng.standard_normal(v2[c.cu_k[2]:c.cu_k[3]].shape).astype(np.float32))
+    o2, l2 = O.varlen_attn(c.q, k2, v2, c.cu_q, c.cu_k, c.scale, True, lib=lib)
+    s = slice(c.cu_q[1], c.cu_q[2])
+    assert np.array_equal(o2[s], out[s]) and np.array_equal(l2[s], lse[s])
+    # reversed order
+    lq, lk = np.diff(c.cu_q)[::-1], np.diff(c.cu_k)[::-1]
+    qr = np.concatenate([c.q[c.cu_q[b]:c.cu_q[b + 1]] for b in reversed(range(3))])
+    kr = np.concatenate([c.k[c.cu_k[b]:c.cu_k[b + 1]] for b in reversed(range(3))])
+    vr = np.concatenate([c.v[c.cu_k[b]:c.cu_k[b + 1]] for b in reversed(range(3))])
+    o3, l3 = O.varlen_attn(qr, kr, vr, cu_from_lengths(lq), cu_from_lengths(lk), c.scale, True, lib=lib)
+    orr = np.concatenate([out[c.cu_q[b]:c.cu_q[b + 1]] for b in reversed(range(3))])
+    lrr = np.concatenate([lse[c.cu_q[b]:c.cu_q[b + 1]] for b in reversed(range(3))])
+    assert np.array_equal(o3, orr) and np.array_equal(l3, lrr)
+
+
+def pin_scale_homogeneity(lib):
+    """softmax(scale * q.k): doubling q (exact in bf16) and halving the scale
+    changes nothing, while doubling only the scale does."""
+    rng = np.random.Generator(np.random.PCG64(18))
+    c = varlen_case("c", [5, 8], [6, 8], 2, 8, 9, False, rng=rng)
+    out, lse = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True, lib=lib)
+    q2 = bf16_bits(bf16_to_f32(c.q) * 2.0)
+    o2, l2 = O.varlen_attn(q2, c.k, c.v, c.cu_q, c.cu_k, c.scale / 2, True, lib=lib)
+    _close(o2, out, 1e-13, "scale homogeneity out")
+    _close(l2, lse, 1e-13, "scale homogeneity lse")
+
+
+def pin_sampled_rows_match_full(lib):
+    """The sampled-row entry point returns exactly the rows of the full pass."""
+    rng = np.random.Generator(np.random.PCG64(19))
+    c = varlen_case("c", [7, 0, 20, 5], [9, 3, 20, 5], 3, 16, 10, True, rng=rng)
+    for causal in (False, True):
+        out, lse = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+        rows = np.array([[t, h] for t in range(0, int(c.cu_q[-1]), 3) for h in range(3)], np.int32)
+        o2, l2 = O.varlen_attn_rows(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, rows, lib=lib)
+        assert np.array_equal(o2, out[rows[:, 0], rows[:, 1]]) and np.array_equal(l2, lse[rows[:, 0], rows[:, 1]])
+
+
+# --- decode pins --------------------------------------------------------------------
+
+def _small_decode(seed, ctx, Hq=4, Hkv=2, D=8, BS=4, max_blocks=None):
+    return decode_case("d", ctx, Hq, Hkv, D, BS, seed, max_blocks=max_blocks)
+
+
+def pin_decode_direct_equals_recurrence(lib):
+    """The direct softmax definition and the decode page's per-token (m, l, o)
+    recurrence with state carried across tiles agree to fp64 rounding."""
+    c = _small_decode(21, [1, 5, 16, 17, 0, 33], max_blocks=10)
+    out = O.paged_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale, lib=lib)
+    for cap in (1, 3, 100):
+        r = O.paged_decode_recurrent(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale, cap, lib=lib)
+        _close(r, out, 1e-12, f"recurrence tile_capacity {cap}")
+
+
+def pin_decode_equals_varlen_single_query(lib):
+    """Decode equals the packed forward pass with one query per sequence on the
+    gathered K/V rows, q head qh reading kv head qh // (Hq / Hkv)."""
+    c = _small_decode(22, [3, 9, 14, 1], Hq=6, Hkv=2, D=16, BS=4)
+    out = O.paged_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale, lib=lib)
+    R = c.num_q_heads // c.num_kv_heads
+    ks, vs = [], []
+    for s in range(c.num_seqs):
+        t = np.arange(c.context_lens[s])
+        blk = c.block_table[s, t // c.block_size]
+        kk = c.k_pool[blk, t % c.block_size]         # [ctx, Hkv, D]
+        vv = c.v_pool[blk, t % c.block_size]
+        ks.append(np.repeat(kk, R, axis=1))          # head qh -> kv head qh // R
+        vs.append(np.repeat(vv, R, axis=1))
+    cu_q = np.arange(c.num_seqs + 1, dtype=np.int32)
+    cu_k = cu_from_lengths(c.context_lens)
+    o2, _ = O.varlen_attn(c.q, np.concatenate(ks), np.concatenate(vs), cu_q, cu_k, c.scale, False, lib=lib)
+    _close(out, o2, 1e-12, "decode vs varlen")
+
+
+def pin_decode_closed_forms(lib):
+    """ctx 0 -> 0; ctx 1 -> v_0; V constant per kv head kh -> every q head of
+    the group qh // (Hq/Hkv) == kh gets that constant."""
+    c = _small_decode(23, [0, 1, 7, 12], Hq=8, Hkv=2, D=8, BS=4)
+    out = O.paged_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale, lib=lib)
+    assert np.all(out[0] == 0.0)
+    v0 = bf16_to_f32(c.v_pool[c.block_table[1, 0], 0]).astype(np.float64)  # [Hkv, D]
+    for qh in range(8):
+        _close(out[1, qh], v0[qh // 4], 1e-14, "ctx 1")
+    vconst = np.zeros(c.v_pool.shape, np.float32)
+    for kh in range(2):
+        vconst[:, :, kh, :] = kh + 1.0
+    out2 = O.paged_decode(c.q, c.k_pool, bf16_bits(vconst), c.block_table, c.context_lens, c.scale, lib=lib)
+    for s in (1, 2, 3):
+        for qh in range(8):
+            _close(out2[s, qh], np.full(8, qh // 4 + 1.0), 1e-13, "gqa grouping")
+
+
+def pin_decode_ignores_tail(lib):
+    """Pool rows past the context length (inside the last block) and table
+    entries past the last used block never reach the result."""
+    c = _small_decode(24, [5, 6, 3], Hq=4, Hkv=2, D=8, BS=4, max_blocks=4)
+    out = O.paged_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale, lib=lib)
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    bt = c.block_table.copy()
+    for s in range(c.num_seqs):
+        ctx = int(c.context_lens[s])
+        last = c.block_table[s, (ctx - 1) // c.block_size]
+        for slot in range(ctx % c.block_size or c.block_size, c.block_size):
+            kp[last, slot] = 0x7FC0  # NaN
+            vp[last, slot] = 0x7FC0
+        bt[s, (ctx + c.block_size - 1) // c.block_size:] = 1 << 30
+    out2 = O.paged_decode(c.q, kp, vp, bt, c.context_lens, c.scale, lib=lib)
+    assert np.array_equal(out, out2)
+    out3 = O.paged_decode_recurrent(c.q, kp, vp, bt, c.context_lens, c.scale, 2, lib=lib)
+    _close(out3, out, 1e-12, "recurrence tail")
+
+
+def pin_decode_gather(lib):
+    """The gather hook equals numpy fancy indexing of the block table."""
+    c = _small_decode(25, [5, 0, 9, 16], Hq=4, Hkv=2, D=8, BS=4, max_blocks=5)
+    dense = O.paged_gather(c.k_pool, c.block_table, c.context_lens, lib=lib)
+    for s in range(c.num_seqs):
+        for t in range(c.max_blocks * c.block_size):
+            if t < c.context_lens[s]:
+                ref = c.k_pool[c.block_table[s, t // c.block_size], t % c.block_size]
+                assert np.array_equal(dense[s, t], ref), (s, t)
+            else:
+                assert np.all(dense[s, t] == 0xFFFF)
+
+
+# --- tile-map pins --------------------------------------------------------------------
+
+def brute_force_tile_map(cu_q, H, BQ):
+    """All (b, qt, h) with qt < ceil(L_b / BQ), sorted by qt descending, then b,
+    then h."""
+    items = []
+    for b in range(len(cu_q) - 1):
+        n = -(-(int(cu_q[b + 1]) - int(cu_q[b])) // BQ)
+        for qt in range(n):
+            for h in range(H):
+                items.append((b, qt, h))
+    items.sort(key=lambda x: (-x[1], x[0], x[2]))
+    return np.array(items, np.int32).reshape(-1, 3)
+
+
+def pin_tile_map(lib):
+    rng = np.random.Generator(np.random.PCG64(26))
+    for trial in range(20):
+        B = int(rng.integers(0, 20))
+        L = rng.integers(0, 700, size=B)
+        cu = cu_from_lengths(L)
+        H = int(rng.integers(1, 5))
+        BQ = int(rng.choice([16, 64, 128]))
+        got = O.varlen_tile_map(cu, H, BQ, lib=lib)
+        ref = brute_force_tile_map(cu, H, BQ)
+        assert np.array_equal(got, ref), (trial, B, H, BQ)
+
+
+ALL_PINS = [
+    pin_bruteforce_tiny,
+    pin_golden_plan_examples,
+    pin_constant_values,
+    pin_single_key,
+    pin_zero_query_uniform,
+    pin_packed_equals_per_sequence,
+    pin_key_permutation,
+    pin_sequence_isolation_and_order,
+    pin_scale_homogeneity,
+    pin_sampled_rows_match_full,
+    pin_decode_direct_equals_recurrence,
+    pin_decode_equals_varlen_single_query,
+    pin_decode_closed_forms,
+    pin_decode_ignores_tail,
+    pin_decode_gather,
+    pin_tile_map,
+]

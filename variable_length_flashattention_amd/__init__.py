@@ -1,0 +1,20 @@
+"""MI355X (gfx950) variable-length FlashAttention forward and paged GQA decode.
+
+The compute lives in ``librra.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/rra.h``).  This package is a thin ctypes binding over it;
+torch supplies device memory and streams only.
+"""
+from .binding import (  # noqa: F401
+    RraError,
+    library_path,
+    load_library,
+    rra_status_string,
+    rra_varlen_attn_fwd,
+    rra_varlen_block_q,
+    rra_paged_decode_attn,
+    rra_paged_decode_workspace_bytes,
+    rra_debug_varlen_tile_map,
+    rra_debug_paged_gather,
+    varlen_attn_fwd,
+    paged_decode_attn,
+)

@@ -1,0 +1,181 @@
+"""ctypes binding of librra.so (argument marshalling only).
+
+Every function named ``rra_*`` forwards to the C entry point of the same name
+declared in ``include/rra.h``.  Tensor arguments may be torch tensors (their
+``data_ptr()`` is passed) or integers (raw device addresses).  ``stream``
+defaults to torch's current stream on the current device.  A non-zero status
+raises :class:`RraError`.  There is no fallback: if the library is missing the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "librra.so"
+_lib = None
+
+RRA_OK = 0
+RRA_ERR_INVALID_ARG = 1
+RRA_ERR_UNSUPPORTED = 2
+RRA_ERR_WORKSPACE = 3
+RRA_ERR_HIP = 4
+
+
+class RraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status} ({rra_status_string(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load librra.so from the package directory (built in-tree)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()'). "
+            "There is no CPU fallback.")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.rra_status_string.argtypes = [i32]
+    lib.rra_status_string.restype = ctypes.c_char_p
+    lib.rra_varlen_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.rra_varlen_attn_fwd.restype = i32
+    lib.rra_varlen_block_q.argtypes = [i32]
+    lib.rra_varlen_block_q.restype = i32
+    lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.rra_paged_decode_attn.restype = i32
+    lib.rra_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.rra_paged_decode_workspace_bytes.restype = sz
+    lib.rra_debug_varlen_tile_map.argtypes = [vp, i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64), vp]
+    lib.rra_debug_varlen_tile_map.restype = i32
+    lib.rra_debug_paged_gather.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.rra_debug_paged_gather.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != RRA_OK:
+        raise RraError(fn, status)
+
+
+def rra_status_string(status: int) -> str:
+    return load_library().rra_status_string(int(status)).decode()
+
+
+def rra_varlen_block_q(head_dim: int) -> int:
+    return int(load_library().rra_varlen_block_q(int(head_dim)))
+
+
+def rra_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, batch, num_heads,
+                        head_dim, softmax_scale, causal, stream=None):
+    st = load_library().rra_varlen_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        int(max_seqlen_q), int(batch), int(num_heads), int(head_dim), float(softmax_scale), int(bool(causal)),
+        _stream(stream))
+    _check("rra_varlen_attn_fwd", st)
+
+
+def rra_paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size) -> int:
+    return int(load_library().rra_paged_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim),
+                                                               int(max_blocks_per_seq), int(block_size)))
+
+
+def rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, num_seqs, num_q_heads, num_kv_heads,
+                          head_dim, block_size, max_blocks_per_seq, softmax_scale, workspace, workspace_bytes,
+                          stream=None):
+    st = load_library().rra_paged_decode_attn(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens), _ptr(out), int(num_seqs),
+        int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size), int(max_blocks_per_seq),
+        float(softmax_scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("rra_paged_decode_attn", st)
+
+
+def rra_debug_varlen_tile_map(cu_seqlens_q, batch, num_heads, max_seqlen_q, head_dim, items_out, capacity,
+                              stream=None) -> int:
+    count = ctypes.c_int64(0)
+    st = load_library().rra_debug_varlen_tile_map(
+        _ptr(cu_seqlens_q), int(batch), int(num_heads), int(max_seqlen_q), int(head_dim), _ptr(items_out),
+        int(capacity), ctypes.byref(count), _stream(stream))
+    _check("rra_debug_varlen_tile_map", st)
+    return int(count.value)
+
+
+def rra_debug_paged_gather(pool, block_table, context_lens, dense, num_seqs, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, stream=None):
+    st = load_library().rra_debug_paged_gather(
+        _ptr(pool), _ptr(block_table), _ptr(context_lens), _ptr(dense), int(num_seqs), int(num_kv_heads),
+        int(head_dim), int(block_size), int(max_blocks_per_seq), _stream(stream))
+    _check("rra_debug_paged_gather", st)
+
+
+# --- allocating conveniences (torch allocates; the library computes) ----------
+
+def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_scale, causal, out=None,
+                    lse=None, stream=None):
+    """q [Tq,H,D], k/v [Tk,H,D] bf16 CUDA tensors; cu_seqlens int32 CUDA
+    tensors.  Returns (out bf16 [Tq,H,D], lse fp32 [Tq,H])."""
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    for t in (q, k, v, cu_seqlens_q, cu_seqlens_k):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous device tensors")
+    if q.dim() != 3 or k.shape != v.shape or k.dim() != 3 or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q must be [Tq,H,D] and k, v [Tk,H,D]")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    Tq, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
+    rra_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, cu_seqlens_q.numel() - 1,
+                        H, D, softmax_scale, causal, stream)
+    return out, lse
+
+
+def paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, softmax_scale, out=None, workspace=None,
+                      stream=None):
+    """q [S,Hq,D] bf16; pools [NB,BS,Hkv,D] bf16; block_table [S,maxb] int32;
+    context_lens [S] int32 (all device tensors).  Returns out bf16 [S,Hq,D]."""
+    import torch
+    S, Hq, D = q.shape
+    _, BS, Hkv, _ = k_pool.shape
+    MB = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = rra_paged_decode_workspace_bytes(S, Hq, D, MB, BS)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, S, Hq, Hkv, D, BS, MB, softmax_scale,
+                          workspace, workspace.numel() * workspace.element_size(), stream)
+    return out
