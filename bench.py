@@ -1,0 +1,238 @@
+"""Benchmark of the varlen attention forward (and the paged decode) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+A step is one rra_varlen_attn_fwd call on the mixed-length workload
+(16 sequences with lengths uniform in [1, 2048] from seed 2001, 32 heads,
+head_dim 128, bf16, causal), inputs resident in HBM.  The value is that
+workload's algorithmic TFLOP/s: 4 * head_dim * heads * (visible query/key
+pairs), causal pairs counted exactly.  The paged GQA decode (64 sequences,
+context lengths uniform in [1, 8192], Hq=32/Hkv=8, head_dim 128, 16-token
+blocks) is timed the same way and reported in GB/s of compulsory HBM bytes.
+The other synthetic workloads are timed once each for context.  Per-launch
+durations come from HIP events recorded on the stream the kernels run on.
+Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--quick", action="store_true", help="skip the context workloads")
+    p.add_argument("--only", default="", help="time only this workload (mixed|decode|...), for profiling")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "variable_length_flashattention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Warm up, then time exactly `steps` launches: wall time bracketed by
+    synchronize, plus per-launch HIP event pairs on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3  # seconds
+    return wall, per
+
+
+class VarlenRun:
+    def __init__(self, torch, case):
+        import variable_length_flashattention_amd as rra
+        self.rra, self.case = rra, case
+        self.q, self.k, self.v = dev_bf16(torch, case.q), dev_bf16(torch, case.k), dev_bf16(torch, case.v)
+        self.cu_q = torch.from_numpy(case.cu_q).cuda()
+        self.cu_k = torch.from_numpy(case.cu_k).cuda()
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        c = self.case
+        self.rra.rra_varlen_attn_fwd(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
+                                     c.max_seqlen_q, c.batch, c.num_heads, c.head_dim, c.scale, c.causal)
+
+
+class DecodeRun:
+    def __init__(self, torch, case):
+        import variable_length_flashattention_amd as rra
+        self.rra, self.case = rra, case
+        self.q = dev_bf16(torch, case.q)
+        self.kp, self.vp = dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)
+        self.bt = torch.from_numpy(case.block_table).cuda()
+        self.cl = torch.from_numpy(case.context_lens).cuda()
+        self.out = torch.empty_like(self.q)
+        need = rra.rra_paged_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
+                                                    case.max_blocks, case.block_size)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        c = self.case
+        self.rra.rra_paged_decode_attn(self.q, self.kp, self.vp, self.bt, self.cl, self.out, c.num_seqs,
+                                       c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks,
+                                       c.scale, self.ws, self.ws.numel())
+
+
+def cpu_baseline(case, n_rows=131072, seed=7):
+    """The fp64 oracle, as it stands, on a bounded random sample of the same
+    workload's (token, head) rows; reported in the metric's unit."""
+    import oracle as O
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Tq = int(case.cu_q[-1])
+    rows = np.stack([rng.integers(0, Tq, n_rows), rng.integers(0, case.num_heads, n_rows)], 1).astype(np.int32)
+    b = np.searchsorted(case.cu_q, rows[:, 0], side="right") - 1
+    i = rows[:, 0] - case.cu_q[b]
+    Lq, Lk = np.diff(case.cu_q)[b], np.diff(case.cu_k)[b]
+    vis = np.clip(i + Lk - Lq + 1, 0, Lk) if case.causal else Lk
+    flops = 4.0 * case.head_dim * float(np.sum(vis))
+    threads = O.default_threads()
+    t0 = time.perf_counter()
+    O.varlen_attn_rows(case.q, case.k, case.v, case.cu_q, case.cu_k, case.scale, case.causal, rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} random (token, head) rows of the mixed workload (seed {seed}); "
+                      f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, fp64"}
+
+
+def load_traffic(name, src_hash):
+    """HBM bytes per launch measured with rocprofv3 counters (scaled by a copy
+    kernel calibration), if the record matches the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards across GPUs only on paper)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from variable_length_flashattention_amd import inputs as I
+    import variable_length_flashattention_amd as rra
+    rra.load_library()
+    src_hash = kernel_source_hash()
+
+    mixed = I.mixed()
+    flops = I.varlen_flops(mixed)
+    run = VarlenRun(torch, mixed)
+    wall, per = time_launches(torch, run, args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (wall / args.steps) / 1e12
+    avg_launch = float(np.mean(per))
+    achieved = flops / avg_launch / 1e12
+    lines = {
+        "metric": "varlen attn fwd TFLOP/s + % bf16 MFMA peak; paged decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mixed-length varlen prefill: 16 sequences, lengths U[1,2048] (seed 2001), "
+                               "q=k lengths, 32 heads, head_dim 128, bf16, causal",
+                   "batch": mixed.batch, "tokens": int(mixed.cu_q[-1]), "num_heads": 32, "head_dim": 128,
+                   "causal": True, "seed": 2001, "flops_per_step": flops, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic("varlen_fwd_mixed", src_hash),
+                     "kernel": "varlen_fwd_kernel<128,true>", "avg_launch_us": round(avg_launch * 1e6, 2),
+                     "median_launch_us": round(float(np.median(per)) * 1e6, 2),
+                     "algorithmic_bytes": I.varlen_bytes(mixed)},
+    }
+
+    # paged decode (second row of the metric)
+    dec = I.paged_decode()
+    drun = DecodeRun(torch, dec)
+    dwall, dper = time_launches(torch, drun, args.steps, args.warmup)
+    dbytes = I.decode_bytes(dec)
+    d_avg = float(np.mean(dper))
+    lines["decode"] = {"workload": "paged GQA decode: 64 seqs, ctx U[1,8192] (seed 5001), Hq=32, Hkv=8, "
+                                   "head_dim 128, 16-token blocks, permuted block table",
+                       "GB/s": round(dbytes / d_avg / 1e9, 1), "frac_of_hbm_peak": round(dbytes / d_avg / 1e9 / PEAK_HBM_GBS, 4),
+                       "avg_call_us": round(d_avg * 1e6, 2), "bytes_per_call": dbytes,
+                       "context_tokens": int(dec.context_lens.sum()),
+                       "note": "split + combine kernels per call; working set exceeds the 256 MiB MALL"}
+    del drun
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        ctx = {}
+        for name, case, bound in [
+            ("tiny_causal", I.tiny(True), "latency"), ("tiny_noncausal", I.tiny(False), "latency"),
+            ("skewed", I.skewed(), "mfma"),
+            ("many_short_d64_causal", I.many_short(64, True), "hbm"),
+            ("many_short_d64_noncausal", I.many_short(64, False), "hbm"),
+            ("many_short_d256_causal", I.many_short(256, True), "hbm"),
+            ("many_short_d256_noncausal", I.many_short(256, False), "hbm"),
+        ]:
+            r = VarlenRun(torch, case)
+            _, p = time_launches(torch, r, 20, 3)
+            t = float(np.mean(p))
+            f, b = I.varlen_flops(case), I.varlen_bytes(case)
+            ctx[name] = {"avg_us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 2),
+                         "frac_mfma_peak": round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "GB/s": round(b / t / 1e9, 1), "frac_hbm_peak": round(b / t / 1e9 / PEAK_HBM_GBS, 4),
+                         "bound": bound}
+            del r
+        lines["other_workloads"] = ctx
+
+    if not args.no_cpu_baseline:
+        lines["cpu_baseline"] = cpu_baseline(mixed)
+    lines["kernel_source_hash"] = src_hash
+    print(json.dumps(lines), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,79 @@
+"""GPU parity of the forward pass against the fp64 oracle (through the C ABI)."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_helpers import compare, run_varlen, sample_rows, say
+from variable_length_flashattention_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_config(causal):
+    """3 packed sequences {1,17,64}, H=2, D=64: every element against the oracle."""
+    c = I.tiny(causal)
+    out, lse = run_varlen(c)
+    ro, rl = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+    compare(out, lse, ro, rl, f"tiny causal={causal}")
+
+
+EDGE_CASES = [
+    # name, q lengths, k lengths, H, D
+    ("ragged_tiles", [1, 127, 128, 129, 300], [1, 127, 128, 129, 300], 2, 128),
+    ("empty_seqs", [0, 5, 0, 0, 70, 0], [0, 5, 3, 0, 70, 9], 3, 64),
+    ("k_longer", [7, 130, 64], [519, 200, 64], 2, 128),
+    ("k_shorter", [40, 200, 129], [5, 64, 1], 2, 128),   # fully masked rows under causal
+    ("k_empty", [10, 3], [0, 4], 1, 64),                 # Lk = 0: no visible key at all
+    ("d256", [1, 33, 160, 64], [1, 33, 170, 64], 2, 256),
+    ("d64_many", list(range(1, 40)), list(range(1, 40)), 1, 64),
+    ("single_long", [700], [700], 1, 128),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[e[0] for e in EDGE_CASES])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_cases(case, causal):
+    name, lq, lk, H, D = case
+    c = I.varlen_case(name, lq, lk, H, D, seed=zlib.crc32(name.encode()) % 10000, causal=causal)
+    out, lse = run_varlen(c)
+    ro, rl = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+    compare(out, lse, ro, rl, f"{name} causal={causal}")
+
+
+def test_scale_and_large_logits():
+    """q scaled x8 and a large softmax scale: peaked rows, max subtraction matters."""
+    c = I.varlen_case("peaked", [33, 200], [33, 260], 2, 128, seed=77, causal=True, q_mult=8.0, scale=0.5)
+    out, lse = run_varlen(c)
+    ro, rl = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True)
+    compare(out, lse, ro, rl, "peaked")
+
+
+FULL = [
+    ("mixed", lambda causal: I.mixed(causal=causal)),
+    ("skewed", lambda causal: I.skewed(causal=causal)),
+    ("many_short_d64", lambda causal: I.many_short(64, causal)),
+    ("many_short_d256", lambda causal: I.many_short(256, causal)),
+]
+
+
+@pytest.mark.parametrize("name,make", FULL, ids=[f[0] for f in FULL])
+@pytest.mark.parametrize("causal", [True, False])
+def test_full_size_sampled(name, make, causal):
+    """Full-size workloads, in the benchmark's launch configuration: every row
+    written and finite (NaN poison before launch), sampled rows against the oracle."""
+    c = make(causal)
+    out, lse = run_varlen(c)
+    assert np.all(np.isfinite(lse)), "some (token, head) row was not written"
+    rows = sample_rows(c)
+    ro, rl = O.varlen_attn_rows(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, rows)
+    compare(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, f"{name} causal={causal} rows={len(rows)}")
+
+
+def test_deterministic():
+    c = I.mixed()
+    a = run_varlen(c)
+    b = run_varlen(c)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -1,0 +1,168 @@
+// C ABI of librra (declared in include/rra.h): host-side validation and
+// kernel launch.  Validation happens before any HIP call; rejected calls
+// launch nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/rra.h"
+#include "rra_internal.h"
+
+using namespace rra;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? RRA_OK : RRA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *rra_status_string(int32_t status)
+{
+    switch (status) {
+    case RRA_OK: return "RRA_OK";
+    case RRA_ERR_INVALID_ARG: return "RRA_ERR_INVALID_ARG";
+    case RRA_ERR_UNSUPPORTED: return "RRA_ERR_UNSUPPORTED";
+    case RRA_ERR_WORKSPACE: return "RRA_ERR_WORKSPACE";
+    case RRA_ERR_HIP: return "RRA_ERR_HIP";
+    default: return "RRA_UNKNOWN_STATUS";
+    }
+}
+
+int32_t rra_varlen_block_q(int32_t head_dim) { return supported_head_dim(head_dim) ? kVarlenBlockQ : 0; }
+
+int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t batch, int32_t num_heads, int32_t head_dim, float softmax_scale,
+                            int32_t causal, void *stream)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0 || max_seqlen_q < 0) return RRA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return RRA_ERR_INVALID_ARG;
+    if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    if (batch == 0 || max_seqlen_q == 0) return RRA_OK;  // no query rows exist
+    if (!q || !out || !lse || !cu_seqlens_q || !cu_seqlens_k) return RRA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return RRA_ERR_INVALID_ARG;
+
+    VarlenArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.batch = batch;
+    a.num_heads = num_heads;
+    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + kVarlenBlockQ - 1) / kVarlenBlockQ;
+    a.n_items = (int64_t)batch * tiles_per_seq * num_heads;
+    a.scale = softmax_scale;
+    a.scale_log2 = softmax_scale * kLog2e;
+    return hip_status(launch_varlen_fwd(a, head_dim, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,
+                                  int32_t max_seqlen_q, int32_t head_dim, int32_t *items_out, int64_t capacity,
+                                  int64_t *item_count, void *stream)
+{
+    if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || !item_count) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return head_dim <= 0 ? RRA_ERR_INVALID_ARG : RRA_ERR_UNSUPPORTED;
+    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + kVarlenBlockQ - 1) / kVarlenBlockQ;
+    const int64_t n = (int64_t)batch * tiles_per_seq * num_heads;
+    *item_count = n;
+    if (n == 0) return RRA_OK;
+    if (!cu_seqlens_q || !items_out || capacity < n) return RRA_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_varlen_tile_map(cu_seqlens_q, batch, num_heads, head_dim, n, items_out, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    return hip_status(e);
+}
+
+size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_blocks_per_seq, int32_t block_size)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq < 0 || block_size <= 0) return 0;
+    return decode_workspace_bytes(num_seqs, num_q_heads, head_dim, decode_n_splits(max_blocks_per_seq, block_size));
+}
+
+static int32_t log2_exact(int32_t x)
+{
+    int32_t s = 0;
+    while ((1 << s) < x) s++;
+    return (1 << s) == x ? s : -1;
+}
+
+int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                              const int32_t *context_lens, void *out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, float softmax_scale, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq < 0)
+        return RRA_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0) return RRA_ERR_INVALID_ARG;
+    if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    const int32_t bs_shift = log2_exact(block_size);
+    if (bs_shift < 0 || block_size > 1024) return RRA_ERR_UNSUPPORTED;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return RRA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return RRA_OK;
+    if (!q || !out || !block_table || !context_lens) return RRA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return RRA_ERR_INVALID_ARG;
+    const int64_t n_splits = decode_n_splits(max_blocks_per_seq, block_size);
+    const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n_splits);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RRA_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_pool = static_cast<const uint16_t *>(k_pool);
+    a.v_pool = static_cast<const uint16_t *>(v_pool);
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint16_t *>(out);
+    const size_t n = (size_t)num_seqs * num_q_heads * n_splits;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_m = reinterpret_cast<float *>(ws);
+    a.ws_l = a.ws_m + n;
+    a.ws_o = reinterpret_cast<float *>(ws + (2 * n * sizeof(float) + 255) / 256 * 256);
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.bs_shift = bs_shift;
+    a.max_blocks = max_blocks_per_seq;
+    a.n_splits = (int32_t)n_splits;
+    const int32_t ratio = num_q_heads / num_kv_heads;
+    a.n_sub = (ratio + 15) / 16;
+    a.scale_log2 = softmax_scale * kLog2e;
+    return hip_status(launch_paged_decode(a, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_debug_paged_gather(const void *pool, const int32_t *block_table, const int32_t *context_lens,
+                               void *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t max_blocks_per_seq, void *stream)
+{
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
+        return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    const int32_t bs_shift = log2_exact(block_size);
+    if (bs_shift < 0 || block_size > 1024) return RRA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || max_blocks_per_seq == 0) return RRA_OK;
+    if (!pool || !block_table || !context_lens || !dense) return RRA_ERR_INVALID_ARG;
+    if (!aligned16(pool) || !aligned16(dense)) return RRA_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 31) return RRA_ERR_INVALID_ARG;
+    return hip_status(launch_paged_gather(static_cast<const uint16_t *>(pool), block_table, context_lens,
+                                          static_cast<uint16_t *>(dense), num_seqs, num_kv_heads, head_dim,
+                                          block_size, bs_shift, max_blocks_per_seq,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels of librra.
+// Wave64 only.  MFMA operand layouts used below (checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16: A lane l holds row l%32, k = 8*(l/32)+e (e<8);
+//     B lane l holds col l%32, same k; C reg r of lane l is
+//     row 8*(r/4) + 4*(l/32) + r%4, col l%32.
+//   v_mfma_f32_16x16x32_bf16: A row l%16, k = 8*(l/16)+e; B col l%16, same k;
+//     C reg r is row 4*(l/16)+r, col l%16.
+//   v_mfma_f32_16x16x16_bf16 (1k): as 16x16x32 with 4 k-elements per lane.
+//   ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address
+//     of 4 consecutive b16 in "row" j/4, columns 4*(j%4)..+3 of a 4x16 tile;
+//     lane i of the group receives column i, rows 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rra {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Round two floats to bf16 (nearest-even) and pack lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    f2 v = {lo, hi};
+    b2 r = __builtin_convertvector(v, b2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+// The two floats a packed bf16 pair represents.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Values of lanes l and l^32 combined (both halves get the result).
+__device__ __forceinline__ float max_across_halves(float x)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                              false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                              false, false);
+    return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x)
+{
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x)
+{
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+__device__ __forceinline__ int wave_max_i32(int x)
+{
+    for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+}  // namespace rra

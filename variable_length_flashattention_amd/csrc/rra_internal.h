@@ -1,0 +1,49 @@
+// Host-side launchers shared between the C ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rra {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Query rows per work item of the forward kernel.
+constexpr int kVarlenBlockQ = 128;
+// Tokens per split of the paged decode.
+constexpr int kDecodeSplitTokens = 256;
+
+struct VarlenArgs {
+    const uint16_t *q, *k, *v;
+    uint16_t *out;
+    float *lse;
+    const int32_t *cu_q, *cu_k;
+    int32_t batch, num_heads;
+    int64_t n_items;     // launched work items (upper bound on real ones)
+    float scale;         // softmax scale
+    float scale_log2;    // softmax scale * log2(e)
+};
+
+hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, hipStream_t stream);
+hipError_t launch_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                  int64_t n_items, int32_t *items_out, hipStream_t stream);
+
+struct DecodeArgs {
+    const uint16_t *q, *k_pool, *v_pool;
+    const int32_t *block_table, *context_lens;
+    uint16_t *out;
+    float *ws_m, *ws_l, *ws_o;
+    int32_t num_seqs, num_q_heads, num_kv_heads;
+    int32_t block_size, bs_shift, max_blocks;
+    int32_t n_splits;    // splits per sequence allocated in the workspace
+    int32_t n_sub;       // q-head subgroups of 16 per kv head
+    float scale_log2;
+};
+
+int64_t decode_n_splits(int32_t max_blocks_per_seq, int32_t block_size);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t n_splits);
+hipError_t launch_paged_decode(const DecodeArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_paged_gather(const uint16_t *pool, const int32_t *block_table, const int32_t *context_lens,
+                               uint16_t *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t bs_shift, int32_t max_blocks, hipStream_t stream);
+
+}  // namespace rra

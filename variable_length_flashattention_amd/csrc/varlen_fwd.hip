@@ -1,0 +1,276 @@
+// Variable-length (packed, cu_seqlens) attention forward for gfx950.
+//
+// Method: "Varlen Flash Attention Implementation Plan", Task 1 (the online
+// softmax over key tiles: running row max m and denominator l in fp32,
+// rescaling of the accumulator, out = acc / l, lse = m + ln l).  The work
+// decomposition, tile shapes and data movement here are this library's own.
+//
+// One workgroup (4 waves) owns a work item (sequence b, query tile qt, head h)
+// of BQ = 128 query rows; wave w owns rows 32w..32w+31 of the tile.  Per key
+// tile of BK keys the workgroup stages K and V in LDS, then each wave
+//   S^T[key][query] = K . Q^T          (v_mfma_f32_32x32x16_bf16, Q in VGPRs)
+//   masks the tail and the causal diagonal (bottom-right: j <= i + Lk - Lq),
+//   updates m and l (exp2 with log2(e) folded into the scale; l sums the fp32
+//   probabilities, the MMA takes them rounded to bf16),
+//   O^T[d][query] += V^T . P^T         (V^T read with ds_read_b64_tr_b16).
+// The S^T orientation puts one query per lane column, so row statistics are
+// lane-local plus one permlane32 swap, and P^T feeds the second MMA straight
+// from the accumulator registers.  Key tiles past the last visible key of a
+// causal tile are never loaded.
+#include "rra_device.h"
+#include "rra_internal.h"
+#include "tile_map.h"
+
+namespace rra {
+
+template <int D>
+struct VarlenTile {
+    static constexpr int BQ = kVarlenBlockQ;
+    static constexpr int BK = D <= 128 ? 64 : 32;
+    static constexpr int KST = D + 8;    // LDS row stride of the K tile (elements)
+    static constexpr int VST = D + 16;   // LDS row stride of the V tile
+    static constexpr int K_ELEMS = BK * KST;
+    static constexpr int V_ELEMS = BK * VST;
+    static constexpr int LDS_INTS = (K_ELEMS + V_ELEMS) / 2;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
+{
+    using T = VarlenTile<D>;
+    constexpr int BQ = T::BQ, BK = T::BK, KST = T::KST, VST = T::VST;
+    constexpr int NC = BK / 32;          // 32-key accumulator tiles per key tile
+    constexpr int NKS = D / 16;          // k-steps of the QK^T MMA
+    constexpr int NDC = D / 32;          // 32-wide d chunks of the output
+    __shared__ __attribute__((aligned(16))) uint16_t smem[T::K_ELEMS + T::V_ELEMS];
+    __shared__ int item[3];
+    uint16_t *Ks = smem;
+    uint16_t *Vs = smem + T::K_ELEMS;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.num_heads;
+    const float sl2 = a.scale_log2;
+
+    for (int64_t w = blockIdx.x; w < a.n_items; w += gridDim.x) {
+        __syncthreads();  // LDS of the previous item no longer in use
+        if (wave == 0) {
+            int b, qt, h;
+            const bool ok = decode_work_item(a.cu_q, a.batch, H, BQ, w, reinterpret_cast<int *>(smem),
+                                             T::LDS_INTS, lane, b, qt, h);
+            if (lane == 0) {
+                item[0] = ok ? b : -1;
+                item[1] = qt;
+                item[2] = h;
+            }
+        }
+        __syncthreads();
+        const int b = item[0];
+        if (b < 0) break;  // items are dense: every later w is past the end too
+        const int qt = item[1], h = item[2];
+
+        const int q0 = a.cu_q[b], k0 = a.cu_k[b];
+        const int Lq = a.cu_q[b + 1] - q0, Lk = a.cu_k[b + 1] - k0;
+        const int diag = Lk - Lq;  // causal: key j visible to query i iff j <= i + diag
+        const int i0 = qt * BQ;
+        const int nrows = min(BQ, Lq - i0);
+        const int iw = i0 + 32 * wave;
+        const int my_i = iw + (lane & 31);
+        const bool row_ok = my_i < Lq;
+        int kend = Lk, kend_w = Lk;
+        if (CAUSAL) {
+            kend = max(0, min(Lk, i0 + nrows + diag));
+            kend_w = max(0, min(Lk, min(iw + 31, Lq - 1) + 1 + diag));
+        }
+        if (32 * wave >= nrows) kend_w = 0;
+        const int nkt = (kend + BK - 1) / BK;
+        const int nkt_w = (kend_w + BK - 1) / BK;
+
+        // Q^T operand: lane holds Q[my_i][16*ks + 8*(lane/32) .. +7]
+        bf16x8 qf[NKS];
+        {
+            const uint16_t *qrow = a.q + ((int64_t)(q0 + my_i) * H + h) * D + 8 * (lane >> 5);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (row_ok) x = load16(qrow + 16 * ks);
+                qf[ks] = as_bf16x8(x);
+            }
+        }
+        f32x16 o[NDC];
+#pragma unroll
+        for (int dc = 0; dc < NDC; dc++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) o[dc][r] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+
+        for (int kt = 0; kt < nkt; kt++) {
+            const int kbase = kt * BK;
+            const int krows = min(BK, Lk - kbase);
+            if (kt > 0) __syncthreads();  // previous K/V tile fully consumed
+            constexpr int CH = BK * D / 8;  // 16-byte chunks per tensor tile
+#pragma unroll
+            for (int c = tid; c < CH; c += 256) {
+                const int row = c / (D / 8), col = c % (D / 8);
+                u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+                if (row < krows) {
+                    const int64_t off = ((int64_t)(k0 + kbase + row) * H + h) * D + col * 8;
+                    kx = load16(a.k + off);
+                    vx = load16(a.v + off);
+                }
+                *reinterpret_cast<u32x4 *>(Ks + row * KST + col * 8) = kx;
+                *reinterpret_cast<u32x4 *>(Vs + row * VST + col * 8) = vx;
+            }
+            __syncthreads();
+            if (kt >= nkt_w) continue;
+
+            // S^T = K Q^T
+            f32x16 s[NC];
+#pragma unroll
+            for (int c = 0; c < NC; c++) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) s[c][r] = 0.f;
+                const uint16_t *kp = Ks + (32 * c + (lane & 31)) * KST + 8 * (lane >> 5);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++) {
+                    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * ks));
+                    s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[c], 0, 0, 0);
+                }
+            }
+            // tail and causal masks (only tiles that need them)
+            const bool need_mask = (kbase + BK > Lk) || (CAUSAL && kbase + BK - 1 > iw + diag);
+            if (need_mask) {
+                const int last = CAUSAL ? min(Lk - 1, my_i + diag) : Lk - 1;
+#pragma unroll
+                for (int c = 0; c < NC; c++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int key = kbase + 32 * c + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        if (key > last) s[c][r] = -INFINITY;
+                    }
+            }
+            // online softmax (row = this lane's query; lanes l and l^32 share it)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < NC; c++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[c][r]);
+            mx = max_across_halves(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2((m_run - m_use) * sl2);
+            const float mc = m_use * sl2;
+            uint32_t pk[NC][8];
+            float rs = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; c++)
+#pragma unroll
+                for (int r2 = 0; r2 < 8; r2++) {
+                    const float p0 = fast_exp2(fmaf(s[c][2 * r2], sl2, -mc));
+                    const float p1 = fast_exp2(fmaf(s[c][2 * r2 + 1], sl2, -mc));
+                    const uint32_t u = pack_bf16x2(p0, p1);
+                    pk[c][r2] = u;
+                    rs += p0 + p1;
+                }
+            rs = sum_across_halves(rs);
+            l_run = alpha * l_run + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int dc = 0; dc < NDC; dc++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) o[dc][r] *= alpha;
+
+            // O^T += V^T P^T, 16 keys per MMA
+            const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+            for (int m = 0; m < BK / 16; m++) {
+                const u32x4 pb = {pk[m >> 1][4 * (m & 1) + 0], pk[m >> 1][4 * (m & 1) + 1],
+                                  pk[m >> 1][4 * (m & 1) + 2], pk[m >> 1][4 * (m & 1) + 3]};
+                const uint16_t *vrow = Vs + (16 * m + 4 * (g >> 1) + (j >> 2)) * VST + 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+                for (int dc = 0; dc < NDC; dc++) {
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 32 * dc));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 8 * VST + 32 * dc));
+                    const u32x4 vv = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+                    o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), o[dc], 0, 0, 0);
+                }
+            }
+        }
+
+        // epilogue: out = O / l (0 when no key is visible), lse = scale*m + ln l (-inf then)
+        if (row_ok) {
+            const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+            uint16_t *orow = a.out + ((int64_t)(q0 + my_i) * H + h) * D + 4 * (lane >> 5);
+#pragma unroll
+            for (int dc = 0; dc < NDC; dc++)
+#pragma unroll
+                for (int rb = 0; rb < 4; rb++) {
+                    const u32x2 pr = {pack_bf16x2(o[dc][4 * rb] * inv_l, o[dc][4 * rb + 1] * inv_l),
+                                      pack_bf16x2(o[dc][4 * rb + 2] * inv_l, o[dc][4 * rb + 3] * inv_l)};
+                    *reinterpret_cast<u32x2 *>(orow + 32 * dc + 8 * rb) = pr;
+                }
+            if (lane < 32)
+                a.lse[(int64_t)(q0 + my_i) * H + h] = l_run > 0.f ? a.scale * m_run + logf(l_run) : -INFINITY;
+        }
+    }
+}
+
+// Test hook: the same work-item decoder, one wave per launched item.
+template <int D>
+__global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q, int32_t batch, int32_t num_heads,
+                                                             int64_t n_items, int32_t *items)
+{
+    __shared__ int nt[VarlenTile<D>::LDS_INTS];
+    const int lane = threadIdx.x;
+    for (int64_t w = blockIdx.x; w < n_items; w += gridDim.x) {
+        int b = -1, qt = -1, h = -1;
+        const bool ok = decode_work_item(cu_q, batch, num_heads, kVarlenBlockQ, w, nt, VarlenTile<D>::LDS_INTS,
+                                         lane, b, qt, h);
+        if (lane == 0) {
+            items[3 * w + 0] = ok ? b : -1;
+            items[3 * w + 1] = ok ? qt : -1;
+            items[3 * w + 2] = ok ? h : -1;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+static unsigned grid_for(int64_t n_items)
+{
+    const int64_t cap = int64_t(1) << 22;
+    return (unsigned)(n_items < cap ? n_items : cap);
+}
+
+template <int D>
+static hipError_t launch_d(const VarlenArgs &a, bool causal, hipStream_t stream)
+{
+    const dim3 grid(grid_for(a.n_items)), block(256);
+    if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((varlen_fwd_kernel<D, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, hipStream_t stream)
+{
+    switch (head_dim) {
+    case 64: return launch_d<64>(a, causal, stream);
+    case 128: return launch_d<128>(a, causal, stream);
+    case 256: return launch_d<256>(a, causal, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                  int64_t n_items, int32_t *items_out, hipStream_t stream)
+{
+    const dim3 grid(grid_for(n_items)), block(64);
+    switch (head_dim) {
+    case 64: hipLaunchKernelGGL(varlen_tile_map_kernel<64>, grid, block, 0, stream, cu_q, batch, num_heads, n_items, items_out); break;
+    case 128: hipLaunchKernelGGL(varlen_tile_map_kernel<128>, grid, block, 0, stream, cu_q, batch, num_heads, n_items, items_out); break;
+    case 256: hipLaunchKernelGGL(varlen_tile_map_kernel<256>, grid, block, 0, stream, cu_q, batch, num_heads, n_items, items_out); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rra
