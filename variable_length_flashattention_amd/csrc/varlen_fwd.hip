@@ -27,25 +27,30 @@ template <int D>
 struct VarlenTile {
     static constexpr int BQ = kVarlenBlockQ;
     static constexpr int BK = D <= 128 ? 64 : 32;
-    static constexpr int KST = D + 8;    // LDS row stride of the K tile (elements)
-    static constexpr int VST = D + 16;   // LDS row stride of the V tile
-    static constexpr int K_ELEMS = BK * KST;
-    static constexpr int V_ELEMS = BK * VST;
-    static constexpr int LDS_INTS = (K_ELEMS + V_ELEMS) / 2;
+    static constexpr int ROWB = D * 2;                 // bytes per K/V row
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BK * ROWB;       // one K (or V) tile
+    static constexpr int WAVE_LOADS = TILE_BYTES / 1024 / 4;  // 1 KiB direct-to-LDS loads per wave per tensor
+    static constexpr int LDS_BYTES = 4 * TILE_BYTES;   // K and V, double-buffered
+    static constexpr int LDS_INTS = LDS_BYTES / 4;
+    // XOR swizzles of the 16-byte chunks of a row (LDS has 32 banks of 4 B):
+    // K is read as 16-byte row pieces of 32 consecutive rows (ds_read_b128),
+    // V as 4 rows x 32 bytes per 16 lanes (ds_read_b64_tr_b16).
+    __device__ static int swz_k(int row) { return row & (CPR < 16 ? CPR - 1 : 15); }
+    __device__ static int swz_v(int row) { return 2 * (row & 3); }
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
+__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(VarlenArgs a)
 {
     using T = VarlenTile<D>;
-    constexpr int BQ = T::BQ, BK = T::BK, KST = T::KST, VST = T::VST;
+    constexpr int BQ = T::BQ, BK = T::BK, ROWB = T::ROWB, TB = T::TILE_BYTES;
     constexpr int NC = BK / 32;          // 32-key accumulator tiles per key tile
     constexpr int NKS = D / 16;          // k-steps of the QK^T MMA
     constexpr int NDC = D / 32;          // 32-wide d chunks of the output
-    __shared__ __attribute__((aligned(16))) uint16_t smem[T::K_ELEMS + T::V_ELEMS];
+    // [buffer][K, V][tile bytes]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
     __shared__ int item[3];
-    uint16_t *Ks = smem;
-    uint16_t *Vs = smem + T::K_ELEMS;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.num_heads;
@@ -55,8 +60,8 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
         __syncthreads();  // LDS of the previous item no longer in use
         if (wave == 0) {
             int b, qt, h;
-            const bool ok = decode_work_item(a.cu_q, a.batch, H, BQ, w, reinterpret_cast<int *>(smem),
-                                             T::LDS_INTS, lane, b, qt, h);
+            const bool ok = decode_work_item(a.cu_q, a.batch, H, BQ, w, reinterpret_cast<int *>(smem), T::LDS_INTS,
+                                             lane, b, qt, h);
             if (lane == 0) {
                 item[0] = ok ? b : -1;
                 item[1] = qt;
@@ -85,6 +90,30 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
         const int nkt = (kend + BK - 1) / BK;
         const int nkt_w = (kend_w + BK - 1) / BK;
 
+        // Direct-to-LDS staging of key tile kt into buffer kt&1.  Wave w
+        // fills 1 KiB blocks w, w+4, ... of each tensor; lane l of a block
+        // writes the 16 bytes at block*1024 + 16*l, i.e. row r, physical
+        // chunk p, which holds logical chunk p ^ swz(r).  Rows past the
+        // sequence end re-read its last row (their scores are masked and
+        // their probabilities are exactly 0).
+        auto stage = [&](int kt) {
+            uint8_t *kb = smem + (kt & 1) * 2 * TB;
+            uint8_t *vb = kb + TB;
+#pragma unroll
+            for (int i = 0; i < T::WAVE_LOADS; i++) {
+                const int blk = i * 4 + wave;
+                const int byte = blk * 1024 + lane * 16;
+                const int row = byte / ROWB, pch = (byte % ROWB) / 16;
+                const int tok = k0 + min(kt * BK + row, Lk - 1);
+                const uint16_t *base = nullptr;
+                const int64_t off = ((int64_t)tok * H + h) * D;
+                base = a.k + off + 8 * (pch ^ T::swz_k(row));
+                __builtin_amdgcn_global_load_lds(base, (__attribute__((address_space(3))) void *)(kb + blk * 1024), 16, 0, 0);
+                base = a.v + off + 8 * (pch ^ T::swz_v(row));
+                __builtin_amdgcn_global_load_lds(base, (__attribute__((address_space(3))) void *)(vb + blk * 1024), 16, 0, 0);
+            }
+        };
+
         // Q^T operand: lane holds Q[my_i][16*ks + 8*(lane/32) .. +7]
         bf16x8 qf[NKS];
         {
@@ -101,27 +130,21 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
         for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
             for (int r = 0; r < 16; r++) o[dc][r] = 0.f;
-        float m_run = -INFINITY, l_run = 0.f;
+        // m_ref: the max the accumulators are currently scaled to; it is only
+        // raised when a row max exceeds it by more than 2^8 in probability
+        // (probabilities stay <= 256, far inside fp32/bf16 range), which
+        // skips most rescales of O.
+        float m_ref = -INFINITY, l_run = 0.f;
 
+        if (nkt > 0) stage(0);
         for (int kt = 0; kt < nkt; kt++) {
             const int kbase = kt * BK;
-            const int krows = min(BK, Lk - kbase);
-            if (kt > 0) __syncthreads();  // previous K/V tile fully consumed
-            constexpr int CH = BK * D / 8;  // 16-byte chunks per tensor tile
-#pragma unroll
-            for (int c = tid; c < CH; c += 256) {
-                const int row = c / (D / 8), col = c % (D / 8);
-                u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-                if (row < krows) {
-                    const int64_t off = ((int64_t)(k0 + kbase + row) * H + h) * D + col * 8;
-                    kx = load16(a.k + off);
-                    vx = load16(a.v + off);
-                }
-                *reinterpret_cast<u32x4 *>(Ks + row * KST + col * 8) = kx;
-                *reinterpret_cast<u32x4 *>(Vs + row * VST + col * 8) = vx;
-            }
-            __syncthreads();
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // tile kt visible; every wave is done with tile kt-1
+            if (kt + 1 < nkt) stage(kt + 1);
             if (kt >= nkt_w) continue;
+            const uint8_t *Kb = smem + (kt & 1) * 2 * TB;
+            const uint8_t *Vb = Kb + TB;
 
             // S^T = K Q^T
             f32x16 s[NC];
@@ -129,10 +152,13 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
             for (int c = 0; c < NC; c++) {
 #pragma unroll
                 for (int r = 0; r < 16; r++) s[c][r] = 0.f;
-                const uint16_t *kp = Ks + (32 * c + (lane & 31)) * KST + 8 * (lane >> 5);
+                const int row = 32 * c + (lane & 31);
+                const uint8_t *kp = Kb + row * ROWB;
+                const int sw = T::swz_k(row);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ks++) {
-                    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * ks));
+                    const int ch = (2 * ks + (lane >> 5)) ^ sw;
+                    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * ch));
                     s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[c], 0, 0, 0);
                 }
             }
@@ -153,12 +179,20 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
 #pragma unroll
             for (int c = 0; c < NC; c++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[c][r]);
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[c][r], s[c][r + 1]));
             mx = max_across_halves(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2((m_run - m_use) * sl2);
-            const float mc = m_use * sl2;
+            const bool raise = mx > m_ref && (m_ref == -INFINITY || (mx - m_ref) * sl2 > 8.f);
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+                l_run *= alpha;
+#pragma unroll
+                for (int dc = 0; dc < NDC; dc++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) o[dc][r] *= alpha;
+                m_ref = m_new;
+            }
+            const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * sl2;
             uint32_t pk[NC][8];
             float rs = 0.f;
 #pragma unroll
@@ -167,17 +201,10 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
                 for (int r2 = 0; r2 < 8; r2++) {
                     const float p0 = fast_exp2(fmaf(s[c][2 * r2], sl2, -mc));
                     const float p1 = fast_exp2(fmaf(s[c][2 * r2 + 1], sl2, -mc));
-                    const uint32_t u = pack_bf16x2(p0, p1);
-                    pk[c][r2] = u;
+                    pk[c][r2] = pack_bf16x2(p0, p1);
                     rs += p0 + p1;
                 }
-            rs = sum_across_halves(rs);
-            l_run = alpha * l_run + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int dc = 0; dc < NDC; dc++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) o[dc][r] *= alpha;
+            l_run += sum_across_halves(rs);
 
             // O^T += V^T P^T, 16 keys per MMA
             const int g = lane >> 4, j = lane & 15;
@@ -185,11 +212,14 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
             for (int m = 0; m < BK / 16; m++) {
                 const u32x4 pb = {pk[m >> 1][4 * (m & 1) + 0], pk[m >> 1][4 * (m & 1) + 1],
                                   pk[m >> 1][4 * (m & 1) + 2], pk[m >> 1][4 * (m & 1) + 3]};
-                const uint16_t *vrow = Vs + (16 * m + 4 * (g >> 1) + (j >> 2)) * VST + 16 * (g & 1) + 4 * (j & 3);
+                const int row = 16 * m + 4 * (g >> 1) + (j >> 2);
+                const int sw = T::swz_v(row);  // rows row and row+8 share it
+                const uint8_t *v0 = Vb + row * ROWB + 8 * (j & 1);
 #pragma unroll
                 for (int dc = 0; dc < NDC; dc++) {
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 32 * dc));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 8 * VST + 32 * dc));
+                    const int ch = (4 * dc + 2 * (g & 1) + ((j & 3) >> 1)) ^ sw;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 16 * ch));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 8 * ROWB + 16 * ch));
                     const u32x4 vv = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
                     o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), o[dc], 0, 0, 0);
@@ -210,7 +240,7 @@ __global__ __launch_bounds__(256) void varlen_fwd_kernel(VarlenArgs a)
                     *reinterpret_cast<u32x2 *>(orow + 32 * dc + 8 * rb) = pr;
                 }
             if (lane < 32)
-                a.lse[(int64_t)(q0 + my_i) * H + h] = l_run > 0.f ? a.scale * m_run + logf(l_run) : -INFINITY;
+                a.lse[(int64_t)(q0 + my_i) * H + h] = l_run > 0.f ? a.scale * m_ref + logf(l_run) : -INFINITY;
         }
     }
 }
