@@ -38,7 +38,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="skip the context workloads")
-    p.add_argument("--only", default="", help="time only this workload (mixed|decode|...), for profiling")
+    p.add_argument("--only", default="", choices=["", "mixed", "decode", "skewed", "many_short_d64",
+                                                  "many_short_d256"],
+                   help="time only this workload (for profiling runs)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="first run one plain device-to-device copy of BYTES bytes (a known-size reference "
+                        "for the HBM byte counters)")
     return p.parse_args()
 
 
@@ -158,6 +163,29 @@ def main():
     import variable_length_flashattention_amd as rra
     rra.load_library()
     src_hash = kernel_source_hash()
+    if args.copy_calibration:
+        n = args.copy_calibration // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.only and args.only != "mixed":
+        case = {"decode": None, "skewed": I.skewed(), "many_short_d64": I.many_short(64, True),
+                "many_short_d256": I.many_short(256, True)}[args.only]
+        if case is None:
+            case = I.paged_decode()
+            r = DecodeRun(torch, case)
+            nbytes, flops = I.decode_bytes(case), I.decode_flops(case)
+        else:
+            r = VarlenRun(torch, case)
+            nbytes, flops = I.varlen_bytes(case), I.varlen_flops(case)
+        _, p = time_launches(torch, r, args.steps, args.warmup)
+        t = float(np.mean(p))
+        print(json.dumps({"only": args.only, "avg_us": round(t * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 2),
+                          "GB/s": round(nbytes / t / 1e9, 1), "kernel_source_hash": src_hash}), flush=True)
+        return
 
     mixed = I.mixed()
     flops = I.varlen_flops(mixed)
@@ -191,6 +219,11 @@ def main():
                      "median_launch_us": round(float(np.median(per)) * 1e6, 2),
                      "algorithmic_bytes": I.varlen_bytes(mixed)},
     }
+
+    if args.only == "mixed":
+        lines["kernel_source_hash"] = src_hash
+        print(json.dumps(lines), flush=True)
+        return
 
     # paged decode (second row of the metric)
     dec = I.paged_decode()

@@ -73,9 +73,10 @@ int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *o
                             int32_t max_seqlen_q, int32_t batch, int32_t num_heads,
                             int32_t head_dim, float softmax_scale, int32_t causal, void *stream);
 
-/* Query rows per work item of rra_varlen_attn_fwd at this head_dim (0 if
- * head_dim is unsupported).  Work items are (sequence, query tile, head). */
-int32_t rra_varlen_block_q(int32_t head_dim);
+/* Query rows per work item of rra_varlen_attn_fwd for this head_dim and
+ * max_seqlen_q (0 if head_dim is unsupported or max_seqlen_q < 0).  Work
+ * items are (sequence, query tile, head). */
+int32_t rra_varlen_block_q(int32_t head_dim, int32_t max_seqlen_q);
 
 /*
  * Paged-KV grouped-query decode attention ([DECODE] AttnState, step_tile_ref,
@@ -123,7 +124,8 @@ size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
  * beyond the last one.  *item_count receives the number of launched items
  * (host value).  items_out must hold 3 * capacity int32; capacity must be at
  * least the launched count, which is batch * ceil(max_seqlen_q / block_q) *
- * num_heads.  block_q = rra_varlen_block_q(head_dim).  Synchronises `stream`.
+ * num_heads with block_q = rra_varlen_block_q(head_dim, max_seqlen_q).
+ * Synchronises `stream`.
  */
 int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,
                                   int32_t max_seqlen_q, int32_t head_dim, int32_t *items_out,

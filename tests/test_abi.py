@@ -51,8 +51,10 @@ def test_status_strings(lib):
 
 
 def test_block_q(lib):
-    assert [rra.rra_varlen_block_q(d) for d in (64, 128, 256)] == [128, 128, 128]
-    assert rra.rra_varlen_block_q(96) == 0
+    assert [rra.rra_varlen_block_q(d, 128) for d in (64, 128, 256)] == [128, 128, 128]
+    assert [rra.rra_varlen_block_q(d, 5000) for d in (64, 128, 256)] == [128, 128, 128]
+    assert rra.rra_varlen_block_q(96, 100) == 0
+    assert rra.rra_varlen_block_q(128, -1) == 0
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced by a rejected call

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def device_tile_map(cu, H, D):
     B = len(cu) - 1
     maxq = int(np.max(np.diff(cu))) if B else 0
-    bq = rra.rra_varlen_block_q(D)
+    bq = rra.rra_varlen_block_q(D, maxq)
     cap = max(1, B * (-(-maxq // bq)) * H)
     items = torch.full((cap * 3,), -7, dtype=torch.int32, device="cuda")
     say(f"  launch rra_debug_varlen_tile_map B={B} H={H} D={D} maxq={maxq}")

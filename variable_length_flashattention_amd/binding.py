@@ -49,7 +49,7 @@ def load_library():
     lib.rra_status_string.restype = ctypes.c_char_p
     lib.rra_varlen_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.rra_varlen_attn_fwd.restype = i32
-    lib.rra_varlen_block_q.argtypes = [i32]
+    lib.rra_varlen_block_q.argtypes = [i32, i32]
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.rra_paged_decode_attn.restype = i32
@@ -89,8 +89,8 @@ def rra_status_string(status: int) -> str:
     return load_library().rra_status_string(int(status)).decode()
 
 
-def rra_varlen_block_q(head_dim: int) -> int:
-    return int(load_library().rra_varlen_block_q(int(head_dim)))
+def rra_varlen_block_q(head_dim: int, max_seqlen_q: int) -> int:
+    return int(load_library().rra_varlen_block_q(int(head_dim), int(max_seqlen_q)))
 
 
 def rra_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, batch, num_heads,

@@ -33,13 +33,16 @@ __device__ __forceinline__ int64_t paged_token_offset(const int32_t *__restrict_
     return ((blk << bs_shift) + slot) * num_kv_heads * head_dim + (int64_t)kh * head_dim;
 }
 
-template <int D>
+// BIG: block_size >= 16, so each group of 16 tokens sits in one pool block
+// and its block id is wave-uniform.
+template <int D, bool BIG>
 __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
 {
     constexpr int NKS = D / 32;   // k-steps of the QK^T MMA (32 d each)
     constexpr int NDC = D / 16;   // 16-wide d chunks of the output
+    constexpr int NV = D / 32;    // 16-byte V pieces per lane per 16 tokens
     constexpr int VST = D + 16;   // LDS row stride of a staged V token
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[4][16 * VST];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[4][2][16 * VST];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
@@ -56,9 +59,41 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     const int col = lane & 15, grp = lane >> 4;
     const bool q_ok = col < nq;
     const int Hkv = a.num_kv_heads;
+    const int bs_shift = a.bs_shift;
     const float sl2 = a.scale_log2;
     const int32_t *bt = a.block_table + (int64_t)s * a.max_blocks;
-    uint16_t *vb = vbuf[wave];
+
+    // Block-table entries covering this split, one per lane (lane j holds the
+    // j-th block from the split's first block; 4 registers cover the 256
+    // blocks a split spans at block_size 1).  Only blocks below
+    // ceil(ctx / block_size) are read.
+    const int blk0 = t_begin >> bs_shift;
+    const int blk_end = ((t_end - 1) >> bs_shift) + 1;
+    constexpr int NBT = BIG ? 1 : 4;
+    int btr[NBT];
+#pragma unroll
+    for (int r = 0; r < NBT; r++) {
+        const int bi = blk0 + lane + 64 * r;
+        btr[r] = bi < blk_end ? bt[bi] : 0;
+    }
+    const int64_t row_elems = (int64_t)Hkv * D;  // elements per pool token row
+    // Element offset of token t (t_begin <= t < t_end), kv head kh.
+    auto token_offset = [&](int t) -> int64_t {
+        const int rel = (t >> bs_shift) - blk0;
+        int blk = __shfl(btr[0], rel & 63, 64);
+        if (!BIG && rel >= 64) {
+            const int b1 = __shfl(btr[NBT > 1 ? 1 : 0], rel & 63, 64), b2 = __shfl(btr[NBT > 2 ? 2 : 0], rel & 63, 64),
+                      b3 = __shfl(btr[NBT > 3 ? 3 : 0], rel & 63, 64);
+            blk = rel < 128 ? b1 : rel < 192 ? b2 : b3;
+        }
+        const int64_t slot = t & ((1 << bs_shift) - 1);
+        return (((int64_t)blk << bs_shift) + slot) * row_elems + (int64_t)kh * D;
+    };
+    // BIG: base offset of group t0's block (uniform) plus the slot's row
+    auto group_base = [&](int t0) -> int64_t {
+        const int blk = __builtin_amdgcn_readlane(btr[0], (t0 >> bs_shift) - blk0);
+        return ((int64_t)blk << bs_shift) * row_elems + (int64_t)kh * D;
+    };
 
     // Q^T operand: lane holds Q[qh0 + col][32*ks + 8*grp .. +7]
     bf16x8 qf[NKS];
@@ -74,72 +109,100 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     f32x4 o[NDC];
 #pragma unroll
     for (int dc = 0; dc < NDC; dc++) o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    // m_ref: the max (per q head, common to all lanes of that column) the
+    // accumulators are scaled to.  It is raised only when some score exceeds
+    // it by more than 2^8 in probability, so most groups need no cross-lane
+    // max.  l_part: this lane's share of the denominator (its 4 tokens per
+    // group), summed across the lane groups once at the end.
+    float m_ref = -INFINITY, l_part = 0.f;
+    const float thresh = 8.f / sl2;  // raw-score headroom above m_ref
+
+    // Loads of one group of 16 tokens: K straight into the MMA A operand
+    // (lane: token t0 + col, d = 32*ks + 8*grp..), V rows for the LDS stage
+    // (lane: token t0 + c/(D/8), 16-byte piece c%(D/8), c = lane + 64 i).
+    // Tokens at or past t_end load nothing and stay zero.
+    u32x4 kr[NKS], vr[NV];
+    // (offsets are computed for every lane, with the token clamped into the
+    // split, so the cross-lane reads of the block table see all lanes)
+    auto load_group = [&](int t0, u32x4 *kd, u32x4 *vd) {
+        const int64_t gb = BIG ? group_base(t0) : 0;
+        const int mask = (1 << bs_shift) - 1;
+        const int t = t0 + col;
+        const int tc = min(t, t_end - 1);
+        const uint16_t *p = a.k_pool + (BIG ? gb + (int64_t)(tc & mask) * row_elems : token_offset(tc)) + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) {
+            kd[ks] = u32x4{0u, 0u, 0u, 0u};
+            if (t < t_end) kd[ks] = load16(p + 32 * ks);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int c = lane + 64 * i;
+            const int tv = t0 + c / (D / 8);
+            const int tvc = min(tv, t_end - 1);
+            const int64_t off = BIG ? gb + (int64_t)(tvc & mask) * row_elems : token_offset(tvc);
+            vd[i] = u32x4{0u, 0u, 0u, 0u};
+            if (tv < t_end) vd[i] = load16(a.v_pool + off + (c % (D / 8)) * 8);
+        }
+    };
+    load_group(t_begin, kr, vr);
 
     for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-        // K operand: lane holds K[t0 + col][32*ks + 8*grp .. +7]
-        bf16x8 kf[NKS];
-        {
-            const int t = t0 + col;
-            if (t < t_end) {
-                const uint16_t *kr = a.k_pool + paged_token_offset(bt, t, a.bs_shift, Hkv, D, kh) + 8 * grp;
+        // issue the next group's loads before working on this one
+        u32x4 kn[NKS], vn[NV];
+        if (t0 + 16 < t_end) load_group(t0 + 16, kn, vn);
+        // stage this group's V rows in the wave's LDS (two buffers, so the
+        // next group's stores never race this group's transposed reads; LDS
+        // operations of one wave complete in order)
+        uint16_t *vb = vbuf[wave][((t0 - t_begin) >> 4) & 1];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ks++) kf[ks] = as_bf16x8(load16(kr + 32 * ks));
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < NKS; ks++) kf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-            }
-        }
-        // stage the 16 V rows (zero past the context) in this wave's LDS
-#pragma unroll
-        for (int i = 0; i < D / 32; i++) {
+        for (int i = 0; i < NV; i++) {
             const int c = lane + 64 * i;
-            const int tt = c / (D / 8), cc = c % (D / 8);
-            const int t = t0 + tt;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (t < t_end) x = load16(a.v_pool + paged_token_offset(bt, t, a.bs_shift, Hkv, D, kh) + cc * 8);
-            *reinterpret_cast<u32x4 *>(vb + tt * VST + cc * 8) = x;
+            *reinterpret_cast<u32x4 *>(vb + (c / (D / 8)) * VST + (c % (D / 8)) * 8) = vr[i];
         }
         // S^T = K Q^T (16 tokens x 16 q heads)
         f32x4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++) sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sv, 0, 0, 0);
+        for (int ks = 0; ks < NKS; ks++)
+            sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[ks]), qf[ks], sv, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; r++)
             if (t0 + 4 * grp + r >= t_end) sv[r] = -INFINITY;
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2((m_run - m_use) * sl2);
-        const float mc = m_use * sl2;
+        const float lmax = max3f(sv[0], sv[1], max3f(sv[2], sv[3], sv[3]));
+        if (__builtin_amdgcn_ballot_w64(lmax > m_ref + thresh || (m_ref == -INFINITY && lmax > -INFINITY))) {
+            float mx = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+            l_part *= alpha;
+#pragma unroll
+            for (int dc = 0; dc < NDC; dc++) o[dc] *= alpha;
+            m_ref = m_new;
+        }
+        const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * sl2;
         const float p0 = fast_exp2(fmaf(sv[0], sl2, -mc)), p1 = fast_exp2(fmaf(sv[1], sl2, -mc));
         const float p2 = fast_exp2(fmaf(sv[2], sl2, -mc)), p3 = fast_exp2(fmaf(sv[3], sl2, -mc));
         const uint32_t u0 = pack_bf16x2(p0, p1), u1 = pack_bf16x2(p2, p3);
-        float rs = (p0 + p1) + (p2 + p3);
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        l_run = alpha * l_run + rs;
-        m_run = m_new;
+        l_part += (p0 + p1) + (p2 + p3);
         const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{u0, u1});
-        // the wave's V stores must land before its transposed reads
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const uint16_t *vrow = vb + (4 * grp + ((lane & 15) >> 2)) * VST + 4 * (lane & 3);
 #pragma unroll
         for (int dc = 0; dc < NDC; dc++) {
-            o[dc] *= alpha;
             const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * dc));
             o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dc], 0, 0, 0);
         }
-        // the transposed reads must complete before the next tokens overwrite vbuf
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) kr[ks] = kn[ks];
+#pragma unroll
+        for (int i = 0; i < NV; i++) vr[i] = vn[i];
     }
+    float l_run = l_part + __shfl_xor(l_part, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
 
     if (q_ok) {
         const int64_t idx = ((int64_t)s * a.num_q_heads + qh0 + col) * a.n_splits + split;
         if (grp == 0) {
-            a.ws_m[idx] = m_run;
+            a.ws_m[idx] = m_ref;
             a.ws_l[idx] = l_run;
         }
         float *op = a.ws_o + idx * D + 4 * grp;
@@ -220,7 +283,8 @@ static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
     const int64_t units = (int64_t)a.num_kv_heads * a.n_sub;
     if (a.n_splits > 0) {
         const dim3 grid((unsigned)((int64_t)a.num_seqs * a.n_splits), (unsigned)((units + 3) / 4)), block(256);
-        hipLaunchKernelGGL(paged_decode_split_kernel<D>, grid, block, 0, stream, a);
+        if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, block, 0, stream, a);
     }
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
     hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);

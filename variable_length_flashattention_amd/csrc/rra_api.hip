@@ -19,6 +19,20 @@ bool supported_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? RRA_OK : RRA_ERR_HIP; }
 
+// Compute units of the current device (queried once per device).
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -35,7 +49,10 @@ const char *rra_status_string(int32_t status)
     }
 }
 
-int32_t rra_varlen_block_q(int32_t head_dim) { return supported_head_dim(head_dim) ? kVarlenBlockQ : 0; }
+int32_t rra_varlen_block_q(int32_t head_dim, int32_t max_seqlen_q)
+{
+    return supported_head_dim(head_dim) && max_seqlen_q >= 0 ? varlen_block_q(head_dim, max_seqlen_q) : 0;
+}
 
 int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
                             const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
@@ -61,11 +78,13 @@ int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *o
     a.cu_k = cu_seqlens_k;
     a.batch = batch;
     a.num_heads = num_heads;
-    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + kVarlenBlockQ - 1) / kVarlenBlockQ;
+    a.block_q = varlen_block_q(head_dim, max_seqlen_q);
+    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + a.block_q - 1) / a.block_q;
+    a.levels = (int32_t)tiles_per_seq;
     a.n_items = (int64_t)batch * tiles_per_seq * num_heads;
     a.scale = softmax_scale;
     a.scale_log2 = softmax_scale * kLog2e;
-    return hip_status(launch_varlen_fwd(a, head_dim, causal == 1, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_varlen_fwd(a, head_dim, causal == 1, device_cus(), static_cast<hipStream_t>(stream)));
 }
 
 int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,
@@ -74,13 +93,15 @@ int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, in
 {
     if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || !item_count) return RRA_ERR_INVALID_ARG;
     if (!supported_head_dim(head_dim)) return head_dim <= 0 ? RRA_ERR_INVALID_ARG : RRA_ERR_UNSUPPORTED;
-    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + kVarlenBlockQ - 1) / kVarlenBlockQ;
+    const int32_t bq = varlen_block_q(head_dim, max_seqlen_q);
+    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + bq - 1) / bq;
     const int64_t n = (int64_t)batch * tiles_per_seq * num_heads;
     *item_count = n;
     if (n == 0) return RRA_OK;
     if (!cu_seqlens_q || !items_out || capacity < n) return RRA_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_varlen_tile_map(cu_seqlens_q, batch, num_heads, head_dim, n, items_out, st);
+    hipError_t e = launch_varlen_tile_map(cu_seqlens_q, cu_seqlens_q, batch, num_heads, bq, (int32_t)tiles_per_seq, n,
+                                          items_out, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     return hip_status(e);
 }

@@ -43,12 +43,22 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __builtin_bi
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max of three floats in one instruction.  Operands are finite or -inf here,
+// so the NaN canonicalisation the compiler would add around fmaxf is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Values of lanes l and l^32 combined (both halves get the result).
 __device__ __forceinline__ float max_across_halves(float x)
 {
     auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
                                               false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+    const float a = __builtin_bit_cast(float, (uint32_t)p[0]), b = __builtin_bit_cast(float, (uint32_t)p[1]);
+    return max3f(a, b, b);
 }
 __device__ __forceinline__ float sum_across_halves(float x)
 {

@@ -7,8 +7,19 @@ namespace rra {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Query rows per work item of the forward kernel.
-constexpr int kVarlenBlockQ = 128;
+// Query rows per work item of the forward kernel: 4 waves x 32 rows.  (An
+// 8-wave, 256-row variant halves the K/V traffic per FLOP but leaves room for
+// only one workgroup per CU, and measured 12-20 % slower on MI355X.)
+inline int varlen_block_q(int head_dim, int max_seqlen_q)
+{
+    (void)head_dim;
+    (void)max_seqlen_q;
+    return 128;
+}
+// LDS ints a forward workgroup sets aside for its work-list tables (enough
+// for about 1700 sequences; more fall back to decoding from global memory).
+constexpr int kSchedInts = 3584;
+
 // Tokens per split of the paged decode.
 constexpr int kDecodeSplitTokens = 256;
 
@@ -18,14 +29,17 @@ struct VarlenArgs {
     float *lse;
     const int32_t *cu_q, *cu_k;
     int32_t batch, num_heads;
-    int64_t n_items;     // launched work items (upper bound on real ones)
+    int32_t block_q;     // query rows per work item (varlen_block_q)
+    int32_t levels;      // ceil(max_seqlen_q / block_q): upper bound on tiles per sequence
+    int64_t n_items;     // batch * levels * num_heads: upper bound on real items
     float scale;         // softmax scale
     float scale_log2;    // softmax scale * log2(e)
 };
 
-hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, hipStream_t stream);
-hipError_t launch_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_heads, int32_t head_dim,
-                                  int64_t n_items, int32_t *items_out, hipStream_t stream);
+hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream);
+hipError_t launch_varlen_tile_map(const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
+                                  int32_t block_q, int32_t levels, int64_t n_items, int32_t *items_out,
+                                  hipStream_t stream);
 
 struct DecodeArgs {
     const uint16_t *q, *k_pool, *v_pool;

@@ -4,12 +4,12 @@
 // by level: level r holds query tile r of every sequence with n_b > r, in
 // ascending b, and levels run from the highest r down to 0.  With a causal
 // mask and Lq == Lk, the tile at level r sees r+1 key tiles, so this order
-// hands out the most expensive tiles first (longest-processing-time first
-// under the hardware's in-order workgroup dispatch).  Each tile is split into
-// num_heads items, head innermost: item w -> tile position w / H, head w % H.
-// When H is a multiple of 8 every item of head h lands on the same XCD
-// (workgroups are dealt round-robin over the 8 XCDs), so all query tiles of a
-// (sequence, head) share one L2.
+// lists the most expensive tiles first.  Each tile is split into num_heads
+// items, head innermost: item w -> tile position w / H, head w % H.
+//
+// With G(x) = sum_b max(0, n_b - x) (the number of tiles at levels >= x), the
+// item's level r is the one with G(r+1) <= w/H < G(r), and its sequence is the
+// (w/H - G(r+1))-th sequence, in ascending b, with n_b > r.
 #pragma once
 #include "rra_device.h"
 
@@ -21,54 +21,98 @@ __device__ __forceinline__ int seq_tiles(const int32_t *__restrict__ cu, int b, 
     return L > 0 ? (L + bq - 1) / bq : 0;
 }
 
-// Executed by all 64 lanes of one wave (wave-uniform control flow).  lds_nt
-// caches n_b when batch <= lds_cap (it may alias other LDS the caller is not
-// using yet).  On return every lane holds the same result.
-__device__ __forceinline__ bool decode_work_item(const int32_t *__restrict__ cu_q, int batch, int num_heads, int bq,
-                                                 int64_t w, int *lds_nt, int lds_cap, int lane, int &b_out,
-                                                 int &qt_out, int &h_out)
-{
-    const bool cached = batch <= lds_cap;
-    int64_t total = 0;
-    int levels = 0;
-    for (int b = lane; b < batch; b += 64) {
-        const int n = seq_tiles(cu_q, b, bq);
-        if (cached) lds_nt[b] = n;
-        total += n;
-        levels = max(levels, n);
-    }
-    total = wave_sum_i64(total);
-    levels = wave_max_i32(levels);
-    // make this wave's LDS writes visible to its own later reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Tables one workgroup builds once in LDS and then decodes any number of
+// items from: cu_seqlens_q and _k copies, and G(x) for x = 0..levels.
+// They are used when 2*(batch+1) + levels + 1 fits the LDS space given;
+// otherwise items are decoded from global memory (decode_work_item_global).
+struct WorkTables {
+    int *cuq, *cuk, *G;  // LDS
+    int batch, levels, bq;
+    bool cached;
+};
 
+// All threads of the workgroup call this; it ends with a barrier.  levels is
+// an upper bound on max_b n_b (ceil(max_seqlen_q / bq)).
+__device__ __forceinline__ WorkTables build_work_tables(const int32_t *__restrict__ cu_q,
+                                                        const int32_t *__restrict__ cu_k, int batch, int bq,
+                                                        int levels, int *lds, int lds_ints)
+{
+    WorkTables t;
+    t.batch = batch;
+    t.bq = bq;
+    t.levels = levels;
+    t.cached = 2 * (batch + 1) + 2 * (levels + 1) <= lds_ints;
+    t.cuq = lds;
+    t.cuk = lds + (batch + 1);
+    int *cnt = lds + 2 * (batch + 1);  // C(y) = #{b : n_b > y}, y = 0..levels
+    t.G = cnt + (levels + 1);
+    if (!t.cached) return t;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int i = tid; i <= batch; i += nt) {
+        t.cuq[i] = cu_q[i];
+        t.cuk[i] = cu_k[i];
+    }
+    for (int y = tid; y <= levels; y += nt) cnt[y] = 0;
+    __syncthreads();
+    // histogram of n_b (cnt[n] += 1), then suffix sums turn it into C(y)
+    for (int b = tid; b < batch; b += nt) {
+        const int n = seq_tiles(t.cuq, b, bq);
+        if (n > 0) atomicAdd(&cnt[min(n, levels)], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // C(y) = sum_{n > y} hist[n]; G(x) = sum_{y >= x} C(y); one wave, serial over
+        // chunks of 64 levels from the top
+        int carry_c = 0, carry_g = 0;
+        for (int top = levels; top >= 0; top -= 64) {
+            const int y = top - tid;
+            const int hist = y >= 0 ? cnt[y] : 0;
+            // inclusive suffix sum of hist over y' >= y within the chunk
+            int s = hist;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(s, off, 64);
+                if (tid >= off) s += o;
+            }
+            const int c_incl = s + carry_c;          // sum_{n >= y} hist[n]
+            const int c_y = c_incl - hist;           // C(y): n > y
+            int g = c_y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(g, off, 64);
+                if (tid >= off) g += o;
+            }
+            const int g_y = g + carry_g;             // sum_{y' >= y} C(y')
+            carry_c = __shfl(c_incl, 63, 64);
+            carry_g = __shfl(g_y, 63, 64);
+            if (y >= 0) {
+                cnt[y] = c_y;
+                t.G[y] = g_y;
+            }
+        }
+    }
+    __syncthreads();
+    return t;
+}
+
+// Decode item w from the LDS tables.  Every lane of a wave gets the same
+// result; any wave may call it independently.  Returns false past the end.
+__device__ __forceinline__ bool decode_work_item_cached(const WorkTables &t, int num_heads, int64_t w, int lane,
+                                                        int &b_out, int &qt_out, int &h_out)
+{
     const int64_t tau = w / num_heads;
     h_out = (int)(w % num_heads);
-    if (tau >= total) return false;
-
-    // G(x) = sum_b max(0, n_b - x): tiles at levels >= x.
-    auto tiles_from = [&](int x) -> int64_t {
-        int64_t s = 0;
-        for (int b = lane; b < batch; b += 64) {
-            const int n = cached ? lds_nt[b] : seq_tiles(cu_q, b, bq);
-            s += max(0, n - x);
-        }
-        return wave_sum_i64(s);
-    };
+    if (tau >= t.G[0]) return false;
     // smallest x in [1, levels] with G(x) <= tau; the item's level is x - 1
-    int lo = 1, hi = levels;
+    int lo = 1, hi = t.levels;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (tiles_from(mid) <= tau) hi = mid;
+        if (t.G[mid] <= tau) hi = mid;
         else lo = mid + 1;
     }
     const int r = lo - 1;
-    int64_t j = tau - tiles_from(lo);  // rank within level r
-    for (int base = 0; base < batch; base += 64) {
+    int64_t j = tau - t.G[lo];  // rank within level r
+    for (int base = 0; base < t.batch; base += 64) {
         const int b = base + lane;
-        const bool pred = b < batch && (cached ? lds_nt[b] : seq_tiles(cu_q, b, bq)) > r;
+        const bool pred = b < t.batch && seq_tiles(t.cuq, b, t.bq) > r;
         const uint64_t mask = __ballot(pred);
         const int cnt = __popcll(mask);
         if (j < cnt) {
@@ -81,6 +125,69 @@ __device__ __forceinline__ bool decode_work_item(const int32_t *__restrict__ cu_
         j -= cnt;
     }
     return false;  // not reached when cu_seqlens is non-decreasing
+}
+
+// The same decode straight from global memory (used when the tables do not
+// fit in LDS).  Executed by all 64 lanes of one wave.
+__device__ __forceinline__ bool decode_work_item_global(const int32_t *__restrict__ cu_q, int batch, int num_heads,
+                                                        int bq, int64_t w, int lane, int &b_out, int &qt_out,
+                                                        int &h_out)
+{
+    int64_t total = 0;
+    int levels = 0;
+    for (int b = lane; b < batch; b += 64) {
+        const int n = seq_tiles(cu_q, b, bq);
+        total += n;
+        levels = max(levels, n);
+    }
+    total = wave_sum_i64(total);
+    levels = wave_max_i32(levels);
+    const int64_t tau = w / num_heads;
+    h_out = (int)(w % num_heads);
+    if (tau >= total) return false;
+    auto tiles_from = [&](int x) -> int64_t {
+        int64_t s = 0;
+        for (int b = lane; b < batch; b += 64) s += max(0, seq_tiles(cu_q, b, bq) - x);
+        return wave_sum_i64(s);
+    };
+    int lo = 1, hi = levels;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (tiles_from(mid) <= tau) hi = mid;
+        else lo = mid + 1;
+    }
+    const int r = lo - 1;
+    int64_t j = tau - tiles_from(lo);
+    for (int base = 0; base < batch; base += 64) {
+        const int b = base + lane;
+        const bool pred = b < batch && seq_tiles(cu_q, b, bq) > r;
+        const uint64_t mask = __ballot(pred);
+        const int cnt = __popcll(mask);
+        if (j < cnt) {
+            const uint64_t below = lane == 0 ? 0ull : (mask & (~0ull >> (64 - lane)));
+            const uint64_t hit = __ballot(pred && (int64_t)__popcll(below) == j);
+            b_out = base + __ffsll((unsigned long long)hit) - 1;
+            qt_out = r;
+            return true;
+        }
+        j -= cnt;
+    }
+    return false;
+}
+
+__device__ __forceinline__ bool decode_work_item(const WorkTables &t, const int32_t *__restrict__ cu_q,
+                                                 int num_heads, int64_t w, int lane, int &b, int &qt, int &h)
+{
+    return t.cached ? decode_work_item_cached(t, num_heads, w, lane, b, qt, h)
+                    : decode_work_item_global(cu_q, t.batch, num_heads, t.bq, w, lane, b, qt, h);
+}
+
+// Item handed to persistent workgroup g (of G) in its k-th round: rounds walk
+// the list in blocks of G items, alternately forwards and backwards, so the
+// costlier-first list is dealt out evenly.
+__device__ __forceinline__ int64_t serpentine_item(int64_t k, int g, int G)
+{
+    return k * G + ((k & 1) ? (G - 1 - g) : g);
 }
 
 }  // namespace rra

@@ -5,9 +5,10 @@
 // rescaling of the accumulator, out = acc / l, lse = m + ln l).  The work
 // decomposition, tile shapes and data movement here are this library's own.
 //
-// One workgroup (4 waves) owns a work item (sequence b, query tile qt, head h)
-// of BQ = 128 query rows; wave w owns rows 32w..32w+31 of the tile.  Per key
-// tile of BK keys the workgroup stages K and V in LDS, then each wave
+// One workgroup of NW waves owns a work item (sequence b, query tile qt,
+// head h) of BQ = 32*NW query rows; each wave owns a 32-row block of the tile.
+// Key tiles of BK keys are staged global->LDS with direct-to-LDS loads,
+// NBUF-deep so that loads run ahead of the compute.  Per key tile each wave
 //   S^T[key][query] = K . Q^T          (v_mfma_f32_32x32x16_bf16, Q in VGPRs)
 //   masks the tail and the causal diagonal (bottom-right: j <= i + Lk - Lq),
 //   updates m and l (exp2 with log2(e) folded into the scale; l sums the fp32
@@ -23,62 +24,69 @@
 
 namespace rra {
 
-template <int D>
+template <int D, int NW>
 struct VarlenTile {
-    static constexpr int BQ = kVarlenBlockQ;
+    static constexpr int BQ = 32 * NW;
     static constexpr int BK = D <= 128 ? 64 : 32;
     static constexpr int ROWB = D * 2;                 // bytes per K/V row
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
     static constexpr int TILE_BYTES = BK * ROWB;       // one K (or V) tile
-    static constexpr int WAVE_LOADS = TILE_BYTES / 1024 / 4;  // 1 KiB direct-to-LDS loads per wave per tensor
-    static constexpr int LDS_BYTES = 4 * TILE_BYTES;   // K and V, double-buffered
+    static constexpr int WAVE_LOADS = TILE_BYTES / 1024 / NW;  // 1 KiB direct-to-LDS loads per wave per tensor
+    static_assert(WAVE_LOADS * 1024 * NW == TILE_BYTES, "tile must split evenly over the waves");
+    // K/V buffers: two tiles, so that two workgroups fit in one CU's LDS
+    // (deeper pipelines at one workgroup per CU measured slower)
+    static constexpr int NBUF = 2;
+    static constexpr int LDS_BYTES = NBUF * 2 * TILE_BYTES;
     static constexpr int LDS_INTS = LDS_BYTES / 4;
     // XOR swizzles of the 16-byte chunks of a row (LDS has 32 banks of 4 B):
     // K is read as 16-byte row pieces of 32 consecutive rows (ds_read_b128),
     // V as 4 rows x 32 bytes per 16 lanes (ds_read_b64_tr_b16).
     __device__ static int swz_k(int row) { return row & (CPR < 16 ? CPR - 1 : 15); }
     __device__ static int swz_v(int row) { return 2 * (row & 3); }
+    __device__ static int row_block(int w) { return w; }
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int MIN_BLOCKS = D <= 128 ? 2 : 1;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(VarlenArgs a)
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__((VarlenTile<D, NW>::THREADS), (VarlenTile<D, NW>::MIN_BLOCKS)) void varlen_fwd_kernel(VarlenArgs a)
 {
-    using T = VarlenTile<D>;
-    constexpr int BQ = T::BQ, BK = T::BK, ROWB = T::ROWB, TB = T::TILE_BYTES;
+    using T = VarlenTile<D, NW>;
+    constexpr int BQ = T::BQ, BK = T::BK, ROWB = T::ROWB, TB = T::TILE_BYTES, NBUF = T::NBUF;
     constexpr int NC = BK / 32;          // 32-key accumulator tiles per key tile
     constexpr int NKS = D / 16;          // k-steps of the QK^T MMA
     constexpr int NDC = D / 32;          // 32-wide d chunks of the output
-    // [buffer][K, V][tile bytes]
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
-    __shared__ int item[3];
+    // K and V tiles, two buffers each, as distinct LDS objects: the compiler
+    // then knows a read of one buffer does not depend on direct-to-LDS loads
+    // still in flight into the other, and does not wait for them.
+    static_assert(NBUF == 2, "the tile loop below alternates two buffers");
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TB];
+    __shared__ int sched[kSchedInts];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.num_heads;
     const float sl2 = a.scale_log2;
+    const int rb = T::row_block(wave);
+    const WorkTables wt = build_work_tables(a.cu_q, a.cu_k, a.batch, BQ, a.levels, sched, kSchedInts);
 
-    for (int64_t w = blockIdx.x; w < a.n_items; w += gridDim.x) {
-        __syncthreads();  // LDS of the previous item no longer in use
-        if (wave == 0) {
-            int b, qt, h;
-            const bool ok = decode_work_item(a.cu_q, a.batch, H, BQ, w, reinterpret_cast<int *>(smem), T::LDS_INTS,
-                                             lane, b, qt, h);
-            if (lane == 0) {
-                item[0] = ok ? b : -1;
-                item[1] = qt;
-                item[2] = h;
-            }
-        }
-        __syncthreads();
-        const int b = item[0];
-        if (b < 0) break;  // items are dense: every later w is past the end too
-        const int qt = item[1], h = item[2];
+    // persistent workgroups: items are dealt out in serpentine order
+    for (int64_t k = 0;; k++) {
+        const int64_t w = serpentine_item(k, blockIdx.x, gridDim.x);
+        if (w >= a.n_items) break;
+        int b, qt, h;
+        if (!decode_work_item(wt, a.cu_q, H, w, lane, b, qt, h)) break;  // the same in every wave
+        __syncthreads();  // LDS buffers of the previous item no longer in use
 
-        const int q0 = a.cu_q[b], k0 = a.cu_k[b];
-        const int Lq = a.cu_q[b + 1] - q0, Lk = a.cu_k[b + 1] - k0;
+        const int *cuq = wt.cached ? wt.cuq : a.cu_q, *cuk = wt.cached ? wt.cuk : a.cu_k;
+        const int q0 = cuq[b], k0 = cuk[b];
+        const int Lq = cuq[b + 1] - q0, Lk = cuk[b + 1] - k0;
         const int diag = Lk - Lq;  // causal: key j visible to query i iff j <= i + diag
         const int i0 = qt * BQ;
         const int nrows = min(BQ, Lq - i0);
-        const int iw = i0 + 32 * wave;
+        const int iw = i0 + 32 * rb;           // first row of this wave
         const int my_i = iw + (lane & 31);
         const bool row_ok = my_i < Lq;
         int kend = Lk, kend_w = Lk;
@@ -86,31 +94,31 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(Varle
             kend = max(0, min(Lk, i0 + nrows + diag));
             kend_w = max(0, min(Lk, min(iw + 31, Lq - 1) + 1 + diag));
         }
-        if (32 * wave >= nrows) kend_w = 0;
+        if (32 * rb >= nrows) kend_w = 0;
         const int nkt = (kend + BK - 1) / BK;
         const int nkt_w = (kend_w + BK - 1) / BK;
 
-        // Direct-to-LDS staging of key tile kt into buffer kt&1.  Wave w
-        // fills 1 KiB blocks w, w+4, ... of each tensor; lane l of a block
+        // Direct-to-LDS staging of key tile kt into buffer kt % NBUF.  Wave w
+        // fills 1 KiB blocks w, w+NW, ... of each tensor; lane l of a block
         // writes the 16 bytes at block*1024 + 16*l, i.e. row r, physical
         // chunk p, which holds logical chunk p ^ swz(r).  Rows past the
         // sequence end re-read its last row (their scores are masked and
         // their probabilities are exactly 0).
-        auto stage = [&](int kt) {
-            uint8_t *kb = smem + (kt & 1) * 2 * TB;
-            uint8_t *vb = kb + TB;
+        auto stage = [&](int kt, uint8_t *kb, uint8_t *vb) {
 #pragma unroll
             for (int i = 0; i < T::WAVE_LOADS; i++) {
-                const int blk = i * 4 + wave;
+                const int blk = i * NW + wave;
                 const int byte = blk * 1024 + lane * 16;
                 const int row = byte / ROWB, pch = (byte % ROWB) / 16;
                 const int tok = k0 + min(kt * BK + row, Lk - 1);
-                const uint16_t *base = nullptr;
                 const int64_t off = ((int64_t)tok * H + h) * D;
-                base = a.k + off + 8 * (pch ^ T::swz_k(row));
-                __builtin_amdgcn_global_load_lds(base, (__attribute__((address_space(3))) void *)(kb + blk * 1024), 16, 0, 0);
-                base = a.v + off + 8 * (pch ^ T::swz_v(row));
-                __builtin_amdgcn_global_load_lds(base, (__attribute__((address_space(3))) void *)(vb + blk * 1024), 16, 0, 0);
+                // (the sources go through named locals: with the address
+                // expression inline as the builtin's argument, the host pass
+                // silently dropped the kernel's launch stub)
+                const uint16_t *ksrc = a.k + off + 8 * (pch ^ T::swz_k(row));
+                const uint16_t *vsrc = a.v + off + 8 * (pch ^ T::swz_v(row));
+                __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void *)(kb + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void *)(vb + blk * 1024), 16, 0, 0);
             }
         };
 
@@ -136,15 +144,14 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(Varle
         // skips most rescales of O.
         float m_ref = -INFINITY, l_run = 0.f;
 
-        if (nkt > 0) stage(0);
-        for (int kt = 0; kt < nkt; kt++) {
+        if (nkt > 0) stage(0, k_lds0, v_lds0);
+        // one key tile; tile kt lives in buffer kt & 1
+        auto tile = [&](int kt, const uint8_t *Kb, const uint8_t *Vb, uint8_t *kn, uint8_t *vn) {
             const int kbase = kt * BK;
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt
             __syncthreads();  // tile kt visible; every wave is done with tile kt-1
-            if (kt + 1 < nkt) stage(kt + 1);
-            if (kt >= nkt_w) continue;
-            const uint8_t *Kb = smem + (kt & 1) * 2 * TB;
-            const uint8_t *Vb = Kb + TB;
+            if (kt + 1 < nkt) stage(kt + 1, kn, vn);
+            if (kt >= nkt_w) return;
 
             // S^T = K Q^T
             f32x16 s[NC];
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(Varle
 #pragma unroll
             for (int c = 0; c < NC; c++)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[c][r], s[c][r + 1]));
+                for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[c][r], s[c][r + 1]);
             mx = max_across_halves(mx);
             const bool raise = mx > m_ref && (m_ref == -INFINITY || (mx - m_ref) * sl2 > 8.f);
             if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -225,6 +232,10 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(Varle
                     o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), o[dc], 0, 0, 0);
                 }
             }
+        };
+        for (int kt = 0; kt < nkt; kt += 2) {
+            tile(kt, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
 
         // epilogue: out = O / l (0 when no key is visible), lse = scale*m + ln l (-inf then)
@@ -234,10 +245,10 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(Varle
 #pragma unroll
             for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
-                for (int rb = 0; rb < 4; rb++) {
-                    const u32x2 pr = {pack_bf16x2(o[dc][4 * rb] * inv_l, o[dc][4 * rb + 1] * inv_l),
-                                      pack_bf16x2(o[dc][4 * rb + 2] * inv_l, o[dc][4 * rb + 3] * inv_l)};
-                    *reinterpret_cast<u32x2 *>(orow + 32 * dc + 8 * rb) = pr;
+                for (int rb4 = 0; rb4 < 4; rb4++) {
+                    const u32x2 pr = {pack_bf16x2(o[dc][4 * rb4] * inv_l, o[dc][4 * rb4 + 1] * inv_l),
+                                      pack_bf16x2(o[dc][4 * rb4 + 2] * inv_l, o[dc][4 * rb4 + 3] * inv_l)};
+                    *reinterpret_cast<u32x2 *>(orow + 32 * dc + 8 * rb4) = pr;
                 }
             if (lane < 32)
                 a.lse[(int64_t)(q0 + my_i) * H + h] = l_run > 0.f ? a.scale * m_ref + logf(l_run) : -INFINITY;
@@ -245,17 +256,17 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void varlen_fwd_kernel(Varle
     }
 }
 
-// Test hook: the same work-item decoder, one wave per launched item.
-template <int D>
-__global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q, int32_t batch, int32_t num_heads,
+// Test hook: the same work tables and decoder, one wave per workgroup.
+__global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
+                                                             int32_t num_heads, int32_t block_q, int32_t levels,
                                                              int64_t n_items, int32_t *items)
 {
-    __shared__ int nt[VarlenTile<D>::LDS_INTS];
+    __shared__ int sched[kSchedInts];
     const int lane = threadIdx.x;
+    const WorkTables wt = build_work_tables(cu_q, cu_k, batch, block_q, levels, sched, kSchedInts);
     for (int64_t w = blockIdx.x; w < n_items; w += gridDim.x) {
         int b = -1, qt = -1, h = -1;
-        const bool ok = decode_work_item(cu_q, batch, num_heads, kVarlenBlockQ, w, nt, VarlenTile<D>::LDS_INTS,
-                                         lane, b, qt, h);
+        const bool ok = decode_work_item(wt, cu_q, num_heads, w, lane, b, qt, h);
         if (lane == 0) {
             items[3 * w + 0] = ok ? b : -1;
             items[3 * w + 1] = ok ? qt : -1;
@@ -265,41 +276,35 @@ __global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q
     }
 }
 
-static unsigned grid_for(int64_t n_items)
+template <int D, int NW>
+static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStream_t stream)
 {
-    const int64_t cap = int64_t(1) << 22;
-    return (unsigned)(n_items < cap ? n_items : cap);
-}
-
-template <int D>
-static hipError_t launch_d(const VarlenArgs &a, bool causal, hipStream_t stream)
-{
-    const dim3 grid(grid_for(a.n_items)), block(256);
-    if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((varlen_fwd_kernel<D, false>), grid, block, 0, stream, a);
+    // persistent grid: as many workgroups as fit on the device at once
+    const int64_t slots = (int64_t)num_cus * VarlenTile<D, NW>::MIN_BLOCKS;
+    const dim3 grid((unsigned)(a.n_items < slots ? a.n_items : slots)), block(64 * NW);
+    if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, NW>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, NW>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, hipStream_t stream)
+hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream)
 {
+    if (a.block_q != 32 * 4) return hipErrorInvalidValue;
     switch (head_dim) {
-    case 64: return launch_d<64>(a, causal, stream);
-    case 128: return launch_d<128>(a, causal, stream);
-    case 256: return launch_d<256>(a, causal, stream);
+    case 64: return launch_d<64, 4>(a, causal, num_cus, stream);
+    case 128: return launch_d<128, 4>(a, causal, num_cus, stream);
+    case 256: return launch_d<256, 4>(a, causal, num_cus, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_heads, int32_t head_dim,
-                                  int64_t n_items, int32_t *items_out, hipStream_t stream)
+hipError_t launch_varlen_tile_map(const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
+                                  int32_t block_q, int32_t levels, int64_t n_items, int32_t *items_out,
+                                  hipStream_t stream)
 {
-    const dim3 grid(grid_for(n_items)), block(64);
-    switch (head_dim) {
-    case 64: hipLaunchKernelGGL(varlen_tile_map_kernel<64>, grid, block, 0, stream, cu_q, batch, num_heads, n_items, items_out); break;
-    case 128: hipLaunchKernelGGL(varlen_tile_map_kernel<128>, grid, block, 0, stream, cu_q, batch, num_heads, n_items, items_out); break;
-    case 256: hipLaunchKernelGGL(varlen_tile_map_kernel<256>, grid, block, 0, stream, cu_q, batch, num_heads, n_items, items_out); break;
-    default: return hipErrorInvalidValue;
-    }
+    const unsigned grid = (unsigned)(n_items < 1024 ? n_items : 1024);
+    hipLaunchKernelGGL(varlen_tile_map_kernel, dim3(grid), dim3(64), 0, stream, cu_q, cu_k, batch, num_heads, block_q,
+                       levels, n_items, items_out);
     return hipGetLastError();
 }
 
