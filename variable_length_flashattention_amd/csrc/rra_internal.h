@@ -7,9 +7,9 @@ namespace rra {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Query rows per work item of the forward kernel: 4 waves x 32 rows.  (An
-// 8-wave, 256-row variant halves the K/V traffic per FLOP but leaves room for
-// only one workgroup per CU, and measured 12-20 % slower on MI355X.)
+// Query rows per work item of the forward kernel: 4 waves x 32 rows.  (Two
+// 32-row blocks per wave halve the LDS operand reads per FLOP but need more
+// than 256 VGPR+AGPR per wave; that variant spilled and ran 2x slower.)
 inline int varlen_block_q(int head_dim, int max_seqlen_q)
 {
     (void)head_dim;
