@@ -120,41 +120,31 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     // Loads of one group of 16 tokens: K straight into the MMA A operand
     // (lane: token t0 + col, d = 32*ks + 8*grp..), V rows for the LDS stage
     // (lane: token t0 + c/(D/8), 16-byte piece c%(D/8), c = lane + 64 i).
-    // Tokens at or past t_end load nothing and stay zero.
-    u32x4 kr[NKS], vr[NV];
-    // (offsets are computed for every lane, with the token clamped into the
-    // split, so the cross-lane reads of the block table see all lanes)
+    // Tokens at or past t_end re-read token t_end-1: their scores are masked
+    // and their probabilities are exactly 0, and the loads stay unconditional
+    // (a conditional load followed by a merge makes the compiler wait for it
+    // on the spot, which would defeat the prefetch).
     auto load_group = [&](int t0, u32x4 *kd, u32x4 *vd) {
         const int64_t gb = BIG ? group_base(t0) : 0;
         const int mask = (1 << bs_shift) - 1;
-        const int t = t0 + col;
-        const int tc = min(t, t_end - 1);
+        const int tc = min(t0 + col, t_end - 1);
         const uint16_t *p = a.k_pool + (BIG ? gb + (int64_t)(tc & mask) * row_elems : token_offset(tc)) + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++) {
-            kd[ks] = u32x4{0u, 0u, 0u, 0u};
-            if (t < t_end) kd[ks] = load16(p + 32 * ks);
-        }
+        for (int ks = 0; ks < NKS; ks++) kd[ks] = load16(p + 32 * ks);
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int c = lane + 64 * i;
-            const int tv = t0 + c / (D / 8);
-            const int tvc = min(tv, t_end - 1);
+            const int tvc = min(t0 + c / (D / 8), t_end - 1);
             const int64_t off = BIG ? gb + (int64_t)(tvc & mask) * row_elems : token_offset(tvc);
-            vd[i] = u32x4{0u, 0u, 0u, 0u};
-            if (tv < t_end) vd[i] = load16(a.v_pool + off + (c % (D / 8)) * 8);
+            vd[i] = load16(a.v_pool + off + (c % (D / 8)) * 8);
         }
     };
-    load_group(t_begin, kr, vr);
 
-    for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-        // issue the next group's loads before working on this one
-        u32x4 kn[NKS], vn[NV];
-        if (t0 + 16 < t_end) load_group(t0 + 16, kn, vn);
+    // Fold one group of 16 tokens into the running state.
+    auto process = [&](int t0, const u32x4 *kr, const u32x4 *vr, uint16_t *vb) {
         // stage this group's V rows in the wave's LDS (two buffers, so the
         // next group's stores never race this group's transposed reads; LDS
         // operations of one wave complete in order)
-        uint16_t *vb = vbuf[wave][((t0 - t_begin) >> 4) & 1];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int c = lane + 64 * i;
@@ -191,10 +181,18 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
             const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * dc));
             o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dc], 0, 0, 0);
         }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ks++) kr[ks] = kn[ks];
-#pragma unroll
-        for (int i = 0; i < NV; i++) vr[i] = vn[i];
+    };
+
+    // Two register sets alternate (no copies between them), so the loads of
+    // the next group are in flight while this one is processed.
+    u32x4 ka[NKS], va_[NV], kb[NKS], vb_[NV];
+    load_group(t_begin, ka, va_);
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+        if (t0 + 16 < t_end) load_group(t0 + 16, kb, vb_);
+        process(t0, ka, va_, vbuf[wave][0]);
+        if (t0 + 16 >= t_end) break;
+        if (t0 + 32 < t_end) load_group(t0 + 32, ka, va_);
+        process(t0 + 16, kb, vb_, vbuf[wave][1]);
     }
     float l_run = l_part + __shfl_xor(l_part, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
