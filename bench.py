@@ -47,10 +47,15 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash():
+VARLEN_SOURCES = ("varlen_fwd.hip", "tile_map.h", "rra_device.h", "rra_internal.h", "rra_api.hip")
+DECODE_SOURCES = ("paged_decode.hip", "rra_device.h", "rra_internal.h", "rra_api.hip")
+
+
+def kernel_source_hash(files=None):
+    """sha256 prefix over the kernel sources (all of csrc/, or the named files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "variable_length_flashattention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -107,8 +112,8 @@ class DecodeRun:
         self.bt = torch.from_numpy(case.block_table).cuda()
         self.cl = torch.from_numpy(case.context_lens).cuda()
         self.out = torch.empty_like(self.q)
-        need = rra.rra_paged_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
-                                                    case.max_blocks, case.block_size)
+        need = rra.rra_paged_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                                    case.head_dim)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
     def __call__(self):
@@ -184,7 +189,9 @@ def main():
         _, p = time_launches(torch, r, args.steps, args.warmup)
         t = float(np.mean(p))
         print(json.dumps({"only": args.only, "avg_us": round(t * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 2),
-                          "GB/s": round(nbytes / t / 1e9, 1), "kernel_source_hash": src_hash}), flush=True)
+                          "GB/s": round(nbytes / t / 1e9, 1), "kernel_source_hash": src_hash,
+                          "varlen_source_hash": kernel_source_hash(VARLEN_SOURCES),
+                          "decode_source_hash": kernel_source_hash(DECODE_SOURCES)}), flush=True)
         return
 
     mixed = I.mixed()
@@ -214,7 +221,7 @@ def main():
                    "causal": True, "seed": 2001, "flops_per_step": flops, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic("varlen_fwd_mixed", src_hash),
+                     "traffic": load_traffic("varlen_fwd_mixed", kernel_source_hash(VARLEN_SOURCES)),
                      "kernel": "varlen_fwd_kernel<128,true>", "avg_launch_us": round(avg_launch * 1e6, 2),
                      "median_launch_us": round(float(np.median(per)) * 1e6, 2),
                      "algorithmic_bytes": I.varlen_bytes(mixed)},
@@ -222,6 +229,7 @@ def main():
 
     if args.only == "mixed":
         lines["kernel_source_hash"] = src_hash
+        lines["varlen_source_hash"] = kernel_source_hash(VARLEN_SOURCES)
         print(json.dumps(lines), flush=True)
         return
 
@@ -235,8 +243,9 @@ def main():
                                    "head_dim 128, 16-token blocks, permuted block table",
                        "GB/s": round(dbytes / d_avg / 1e9, 1), "frac_of_hbm_peak": round(dbytes / d_avg / 1e9 / PEAK_HBM_GBS, 4),
                        "avg_call_us": round(d_avg * 1e6, 2), "bytes_per_call": dbytes,
+                       "traffic": load_traffic("paged_decode", kernel_source_hash(DECODE_SOURCES)),
                        "context_tokens": int(dec.context_lens.sum()),
-                       "note": "split + combine kernels per call; working set exceeds the 256 MiB MALL"}
+                       "note": "offsets + range + combine kernels per call; working set exceeds the 256 MiB MALL"}
     del drun
     torch.cuda.empty_cache()
 

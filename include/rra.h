@@ -96,11 +96,14 @@ int32_t rra_varlen_block_q(int32_t head_dim, int32_t max_seqlen_q);
  *   block_size    power of two in [1, 1024]
  *   softmax_scale finite and > 0
  *   workspace     device buffer of at least rra_paged_decode_workspace_bytes(...)
- *                 bytes (fp32 partial softmax state of each split), owned by the
- *                 caller; its contents on entry do not matter
+ *                 bytes (fp32 partial softmax states), owned by the caller; its
+ *                 contents on entry do not matter
  * out = sum_t softmax_t(softmax_scale * q . K_t) V_t over t < context_lens[s],
- * and out = 0 for a sequence with context length 0.  Two kernels run on
- * `stream`: per-split partial state, then a combine that writes out.
+ * and out = 0 for a sequence with context length 0.  Context lengths
+ * outside [0, max_blocks_per_seq*block_size] are clamped into it, and the sum
+ * over sequences of ceil(ctx / 16) must stay below 2^31.  Three kernels run
+ * on `stream`: the token-group offsets of the sequences, the partial states
+ * of equal ranges of token groups, then a combine that writes out.
  */
 int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *block_table, const int32_t *context_lens, void *out,
@@ -110,9 +113,12 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
                               void *stream);
 
 /* Workspace bytes rra_paged_decode_attn needs for these sizes (0 if the sizes
- * are invalid). */
-size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                        int32_t max_blocks_per_seq, int32_t block_size);
+ * are invalid or head_dim is unsupported).  It does not depend on the context
+ * lengths or the block size: the contexts are cut into a fixed number of
+ * equal ranges, and the workspace holds one partial state per (range,
+ * sequence) piece bound plus the sequences' token-group offsets. */
+size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim);
 
 /*
  * Test hooks (integer work, checked bit-exactly against an independent

@@ -102,12 +102,24 @@ def test_decode_validation(lib, kw, status):
 
 
 def test_workspace_size(lib):
-    # splits of 256 tokens: 512 blocks of 16 -> 32 splits; (m, l) then o, fp32
-    n = 64 * 32 * 32
-    ml = (2 * n * 4 + 255) // 256 * 256
-    assert rra.rra_paged_decode_workspace_bytes(64, 32, 128, 512, 16) == ml + n * 128 * 4
-    assert rra.rra_paged_decode_workspace_bytes(-1, 32, 128, 512, 16) == 0
-    assert rra.rra_paged_decode_workspace_bytes(4, 8, 64, 0, 16) == 0 + 0  # no splits
+    # The contexts are cut into 4096 / 2048 / 1024 ranges of token groups at
+    # head_dim 64 / 128 / 256, shared among the kv-head units (a unit is one
+    # kv head and up to 16 of its q heads).  Layout: goff int32[S+1] | m, l
+    # fp32[slots*Hq] | o fp32[slots*Hq*D], slots = ranges/units + S, parts on
+    # 256-byte boundaries.
+    def expect(S, Hq, Hkv, D):
+        units = Hkv * -(-(Hq // Hkv) // 16)
+        ranges = max(1, {64: 4096, 128: 2048, 256: 1024}[D] // units)
+        n = (ranges + S) * Hq
+        up = lambda x: -(-x // 256) * 256
+        return up((S + 1) * 4) + up(2 * n * 4) + n * D * 4
+    assert expect(64, 32, 8, 128) == 512 + 81920 + 10240 * 128 * 4
+    for args in [(64, 32, 8, 128), (1, 8, 8, 64), (0, 4, 1, 256), (4096, 64, 1, 128), (3, 128, 2, 64)]:
+        assert rra.rra_paged_decode_workspace_bytes(*args) == expect(*args), args
+    assert rra.rra_paged_decode_workspace_bytes(-1, 32, 8, 128) == 0
+    assert rra.rra_paged_decode_workspace_bytes(4, 6, 4, 64) == 0   # Hq not a multiple of Hkv
+    assert rra.rra_paged_decode_workspace_bytes(4, 8, 0, 64) == 0
+    assert rra.rra_paged_decode_workspace_bytes(4, 8, 8, 80) == 0   # unsupported head_dim
 
 
 def test_debug_tile_map_validation(lib):

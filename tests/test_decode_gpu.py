@@ -16,7 +16,7 @@ def run_decode(c, poison=True):
     out = torch.empty_like(q)
     if poison:
         out.view(torch.int16).fill_(0x7FC0)
-    need = rra.rra_paged_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim, c.max_blocks, c.block_size)
+    need = rra.rra_paged_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim)
     ws = torch.full((max(need, 16),), 0x7F, dtype=torch.uint8, device="cuda")  # garbage on entry is fine
     say(f"  launch rra_paged_decode_attn case={c.name} seed={c.seed} S={c.num_seqs} Hq={c.num_q_heads} "
         f"Hkv={c.num_kv_heads} D={c.head_dim} BS={c.block_size} maxb={c.max_blocks}")
@@ -48,6 +48,16 @@ CASES = [
     ("bs8", [90, 7], 8, 2, 256, 8),
     ("bs64", [1000, 130], 8, 2, 128, 64),
     ("all_empty", [0, 0], 4, 2, 128, 16),
+    # The contexts are cut into equal ranges of 16-token groups (4096 / 2048 /
+    # 1024 ranges at head_dim 64 / 128 / 256, shared by the kv-head units of
+    # one kv head and up to 16 q heads); these cases place range and chunk
+    # boundaries where the schedule has to get them right.
+    ("many_short_seqs", np.random.Generator(np.random.PCG64(77)).integers(0, 61, 700).tolist(), 8, 8, 64, 16),
+    ("long_and_short", [20000] + [5] * 200 + [0, 33], 32, 8, 128, 16),
+    ("one_long_tiny_ranges", [100000], 8, 1, 64, 16),             # 2 groups per range
+    ("bs1_multi_chunk", [20000, 3], 1024, 1, 64, 1),             # 320 tokens per range
+    ("bs16_multi_chunk", [36000, 100, 0], 2048, 1, 64, 16),      # 1136 tokens per range
+    ("d256_ranges", [3000, 1, 4500], 64, 4, 256, 32),
 ]
 
 

@@ -53,7 +53,7 @@ def load_library():
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.rra_paged_decode_attn.restype = i32
-    lib.rra_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.rra_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.rra_paged_decode_workspace_bytes.restype = sz
     lib.rra_debug_varlen_tile_map.argtypes = [vp, i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64), vp]
     lib.rra_debug_varlen_tile_map.restype = i32
@@ -102,9 +102,9 @@ def rra_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     _check("rra_varlen_attn_fwd", st)
 
 
-def rra_paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size) -> int:
-    return int(load_library().rra_paged_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim),
-                                                               int(max_blocks_per_seq), int(block_size)))
+def rra_paged_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
+    return int(load_library().rra_paged_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(num_kv_heads),
+                                                               int(head_dim)))
 
 
 def rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, num_seqs, num_q_heads, num_kv_heads,
@@ -173,7 +173,7 @@ def paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, softmax_scal
     MB = block_table.shape[1]
     if out is None:
         out = torch.empty_like(q)
-    need = rra_paged_decode_workspace_bytes(S, Hq, D, MB, BS)
+    need = rra_paged_decode_workspace_bytes(S, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, S, Hq, Hkv, D, BS, MB, softmax_scale,

@@ -3,17 +3,27 @@
 // Method: "spark_storage/attention_ref.rs" -- the decode state (m, l, o) in
 // fp32 (AttnState), its update over the tokens of a list of pool blocks
 // (step_tile_ref; the state is carried from one block list to the next), and
-// the guarded finalize out = o / l, 0 when l == 0 (finalize_ref).  Here the
-// context of each sequence is cut into splits of 256 tokens; one wave folds a
-// split into a partial state for one kv head and its group of q heads, and a
-// second kernel merges the partial states of a sequence and finalizes.
+// the guarded finalize out = o / l, 0 when l == 0 (finalize_ref).
 //
-// Split kernel, per 16 tokens:
+// Schedule: the contexts of all sequences, cut into groups of 16 tokens and
+// laid end to end, are split into n_ranges equal ranges of groups.  One wave
+// owns one range for one kv head (and its group of up to 16 q heads), so
+// every wave streams the same number of K/V bytes however the context
+// lengths are distributed.  A range that covers pieces of several sequences
+// folds each piece into its own partial state; the piece of sequence s in
+// range w is stored in partial slot w + s (two pieces (w, s) and (w', s')
+// with w + s == w' + s' cannot both exist, since ranges and sequences are
+// both in order).  A combine kernel merges the pieces of each sequence and
+// finalizes.  A first tiny kernel writes the group offsets of the sequences
+// (an exclusive prefix sum of ceil(ctx / 16)) into the workspace.
+//
+// Per 16 tokens a wave computes
 //   S^T[token][q head] = K . Q^T     (v_mfma_f32_16x16x32_bf16; K straight
 //                                     from the pool into the A operand)
-//   online softmax per q head (max/sum over 4 registers x 4 lane groups)
+//   the online softmax per q head (cross-lane max only when a score exceeds
+//   the running reference max by more than 2^8 in probability),
 //   O^T[d][q head] += V^T . P^T      (v_mfma_f32_16x16x16_bf16; V staged in
-//                                     wave-private LDS, read transposed)
+//                                     wave-private LDS, read transposed).
 // Only tokens t < context_lens[s] are read; the block table is never read at
 // or past ceil(ctx / block_size).
 #include "rra_device.h"
@@ -21,7 +31,7 @@
 
 namespace rra {
 
-constexpr int kSplit = kDecodeSplitTokens;
+constexpr int kGroup = 16;  // tokens per MMA step
 
 // Element offset of (token t, kv head kh) of a sequence whose block-table row
 // is bt.  block_size = 1 << bs_shift.
@@ -33,6 +43,54 @@ __device__ __forceinline__ int64_t paged_token_offset(const int32_t *__restrict_
     return ((blk << bs_shift) + slot) * num_kv_heads * head_dim + (int64_t)kh * head_dim;
 }
 
+// Context length as the kernels use it: clamped to [0, max_blocks * block_size]
+// so that no block-table entry past the row is read.
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int bs_shift)
+{
+    return min(max(ctx, 0), max_blocks << bs_shift);
+}
+
+// Group offsets goff[s] = sum_{s' < s} ceil(ctx_s' / 16), s = 0..S, into the
+// workspace (one workgroup).
+__global__ __launch_bounds__(256) void paged_decode_offsets_kernel(const int32_t *context_lens, int32_t num_seqs,
+                                                                   int32_t max_blocks, int32_t bs_shift,
+                                                                   int32_t *goff)
+{
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int base = 0; base < num_seqs; base += 256) {
+        const int s = base + tid;
+        const int ctx = s < num_seqs ? clamp_ctx(context_lens[s], max_blocks, bs_shift) : 0;
+        const int g = (ctx + kGroup - 1) / kGroup;
+        int x = g;  // inclusive scan within the wave
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int before = carry;
+        for (int w = 0; w < wave; w++) before += wsum[w];
+        if (s < num_seqs) goff[s] = before + x - g;
+        carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
+    }
+    if (tid == 0) goff[num_seqs] = carry;
+}
+
+// first s in [0, S) with goff[s + 1] > g (g < goff[S])
+__device__ __forceinline__ int seq_of_group(const int32_t *__restrict__ goff, int S, int g)
+{
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (goff[mid + 1] > g) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
 // BIG: block_size >= 16, so each group of 16 tokens sits in one pool block
 // and its block id is wave-uniform.
 template <int D, bool BIG>
@@ -42,17 +100,22 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     constexpr int NDC = D / 16;   // 16-wide d chunks of the output
     constexpr int NV = D / 32;    // 16-byte V pieces per lane per 16 tokens
     constexpr int VST = D + 16;   // LDS row stride of a staged V token
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[4][2][16 * VST];
+    constexpr int NBT = BIG ? 1 : 4;  // registers of block-table entries per lane
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[4][2][kGroup * VST];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int s = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int unit = blockIdx.y * 4 + wave;
     if (unit >= a.num_kv_heads * a.n_sub) return;  // no block-level barriers below
     const int kh = unit / a.n_sub, sub = unit % a.n_sub;
-    const int ctx = a.context_lens[s];
-    const int t_begin = split * kSplit;
-    if (t_begin >= ctx) return;
-    const int t_end = min(ctx, t_begin + kSplit);
+    const int S = a.num_seqs;
+    const int32_t *goff = a.ws_goff;
+    const int G = goff[S];
+    const int P = G / a.n_ranges + (G % a.n_ranges != 0);  // groups per range
+    const int64_t g_lo64 = (int64_t)blockIdx.x * P;
+    if (g_lo64 >= G) return;
+    const int g_lo = (int)g_lo64;
+    const int g_hi = (int)min((int64_t)G, g_lo64 + P);
+
     const int ratio = a.num_q_heads / a.num_kv_heads;
     const int qh0 = kh * ratio + 16 * sub;
     const int nq = min(16, ratio - 16 * sub);
@@ -61,157 +124,160 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     const int Hkv = a.num_kv_heads;
     const int bs_shift = a.bs_shift;
     const float sl2 = a.scale_log2;
-    const int32_t *bt = a.block_table + (int64_t)s * a.max_blocks;
+    const float thresh = 8.f / sl2;                // raw-score headroom above the reference max
+    const int64_t row_elems = (int64_t)Hkv * D;    // elements per pool token row
 
-    // Block-table entries covering this split, one per lane (lane j holds the
-    // j-th block from the split's first block; 4 registers cover the 256
-    // blocks a split spans at block_size 1).  Only blocks below
-    // ceil(ctx / block_size) are read.
-    const int blk0 = t_begin >> bs_shift;
-    const int blk_end = ((t_end - 1) >> bs_shift) + 1;
-    constexpr int NBT = BIG ? 1 : 4;
-    int btr[NBT];
-#pragma unroll
-    for (int r = 0; r < NBT; r++) {
-        const int bi = blk0 + lane + 64 * r;
-        btr[r] = bi < blk_end ? bt[bi] : 0;
-    }
-    const int64_t row_elems = (int64_t)Hkv * D;  // elements per pool token row
-    // Element offset of token t (t_begin <= t < t_end), kv head kh.
-    auto token_offset = [&](int t) -> int64_t {
-        const int rel = (t >> bs_shift) - blk0;
-        int blk = __shfl(btr[0], rel & 63, 64);
-        if (!BIG && rel >= 64) {
-            const int b1 = __shfl(btr[NBT > 1 ? 1 : 0], rel & 63, 64), b2 = __shfl(btr[NBT > 2 ? 2 : 0], rel & 63, 64),
-                      b3 = __shfl(btr[NBT > 3 ? 3 : 0], rel & 63, 64);
-            blk = rel < 128 ? b1 : rel < 192 ? b2 : b3;
-        }
-        const int64_t slot = t & ((1 << bs_shift) - 1);
-        return (((int64_t)blk << bs_shift) + slot) * row_elems + (int64_t)kh * D;
-    };
-    // BIG: base offset of group t0's block (uniform) plus the slot's row
-    auto group_base = [&](int t0) -> int64_t {
-        const int blk = __builtin_amdgcn_readlane(btr[0], (t0 >> bs_shift) - blk0);
-        return ((int64_t)blk << bs_shift) * row_elems + (int64_t)kh * D;
-    };
+    for (int s = seq_of_group(goff, S, g_lo); s < S && goff[s] < g_hi; s++) {
+        const int gs0 = goff[s];
+        const int ctx = clamp_ctx(a.context_lens[s], a.max_blocks, bs_shift);
+        const int seg_begin = kGroup * (max(g_lo, gs0) - gs0);
+        const int seg_end = min(ctx, kGroup * (min(g_hi, goff[s + 1]) - gs0));
+        if (seg_begin >= seg_end) continue;
+        const int32_t *bt = a.block_table + (int64_t)s * a.max_blocks;
 
-    // Q^T operand: lane holds Q[qh0 + col][32*ks + 8*grp .. +7]
-    bf16x8 qf[NKS];
-    {
-        const uint16_t *qrow = a.q + ((int64_t)s * a.num_q_heads + qh0 + col) * D + 8 * grp;
+        // Q^T operand: lane holds Q[qh0 + col][32*ks + 8*grp .. +7]
+        bf16x8 qf[NKS];
+        {
+            const uint16_t *qrow = a.q + ((int64_t)s * a.num_q_heads + qh0 + (q_ok ? col : 0)) * D + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (q_ok) x = load16(qrow + 32 * ks);
-            qf[ks] = as_bf16x8(x);
+            for (int ks = 0; ks < NKS; ks++) qf[ks] = as_bf16x8(load16(qrow + 32 * ks));
         }
-    }
-    f32x4 o[NDC];
+        f32x4 o[NDC];
 #pragma unroll
-    for (int dc = 0; dc < NDC; dc++) o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // m_ref: the max (per q head, common to all lanes of that column) the
-    // accumulators are scaled to.  It is raised only when some score exceeds
-    // it by more than 2^8 in probability, so most groups need no cross-lane
-    // max.  l_part: this lane's share of the denominator (its 4 tokens per
-    // group), summed across the lane groups once at the end.
-    float m_ref = -INFINITY, l_part = 0.f;
-    const float thresh = 8.f / sl2;  // raw-score headroom above m_ref
+        for (int dc = 0; dc < NDC; dc++) o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // m_ref: the max (per q head, common to all lanes of that column) the
+        // accumulators are scaled to; l_part: this lane's share of the
+        // denominator (its 4 tokens per group), summed across lanes at the end.
+        float m_ref = -INFINITY, l_part = 0.f;
 
-    // Loads of one group of 16 tokens: K straight into the MMA A operand
-    // (lane: token t0 + col, d = 32*ks + 8*grp..), V rows for the LDS stage
-    // (lane: token t0 + c/(D/8), 16-byte piece c%(D/8), c = lane + 64 i).
-    // Tokens at or past t_end re-read token t_end-1: their scores are masked
-    // and their probabilities are exactly 0, and the loads stay unconditional
-    // (a conditional load followed by a merge makes the compiler wait for it
-    // on the spot, which would defeat the prefetch).
-    auto load_group = [&](int t0, u32x4 *kd, u32x4 *vd) {
-        const int64_t gb = BIG ? group_base(t0) : 0;
-        const int mask = (1 << bs_shift) - 1;
-        const int tc = min(t0 + col, t_end - 1);
-        const uint16_t *p = a.k_pool + (BIG ? gb + (int64_t)(tc & mask) * row_elems : token_offset(tc)) + 8 * grp;
+        // the piece in chunks whose blocks fit the lanes' block-table registers
+        for (int c_begin = seg_begin; c_begin < seg_end;) {
+            const int blk0 = c_begin >> bs_shift;
+            const int t_end = (int)min((int64_t)seg_end, (int64_t)(blk0 + 64 * NBT) << bs_shift);
+            const int blk_end = ((t_end - 1) >> bs_shift) + 1;
+            int btr[NBT];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++) kd[ks] = load16(p + 32 * ks);
+            for (int r = 0; r < NBT; r++) {
+                const int bi = blk0 + lane + 64 * r;
+                btr[r] = bi < blk_end ? bt[bi] : 0;
+            }
+            // Element offset of token t (c_begin <= t < t_end), kv head kh.
+            auto token_offset = [&](int t) -> int64_t {
+                const int rel = (t >> bs_shift) - blk0;
+                int blk = __shfl(btr[0], rel & 63, 64);
+                if (!BIG && rel >= 64) {
+                    const int b1 = __shfl(btr[NBT > 1 ? 1 : 0], rel & 63, 64),
+                              b2 = __shfl(btr[NBT > 2 ? 2 : 0], rel & 63, 64),
+                              b3 = __shfl(btr[NBT > 3 ? 3 : 0], rel & 63, 64);
+                    blk = rel < 128 ? b1 : rel < 192 ? b2 : b3;
+                }
+                const int64_t slot = t & ((1 << bs_shift) - 1);
+                return (((int64_t)blk << bs_shift) + slot) * row_elems + (int64_t)kh * D;
+            };
+            // BIG: base offset of group t0's block (uniform)
+            auto group_base = [&](int t0) -> int64_t {
+                const int blk = __builtin_amdgcn_readlane(btr[0], (t0 >> bs_shift) - blk0);
+                return ((int64_t)blk << bs_shift) * row_elems + (int64_t)kh * D;
+            };
+            // Loads of one group: K straight into the MMA A operand (lane:
+            // token t0 + col, d = 32*ks + 8*grp..), V rows for the LDS stage
+            // (lane: token t0 + c/(D/8), 16-byte piece c%(D/8), c = lane + 64 i).
+            // Tokens at or past t_end re-read token t_end-1: their scores are
+            // masked and their probabilities are exactly 0, and the loads stay
+            // unconditional (a conditional load merged with a default makes the
+            // compiler wait for it on the spot, defeating the prefetch).
+            auto load_group = [&](int t0, u32x4 *kd, u32x4 *vd) {
+                const int64_t gb = BIG ? group_base(t0) : 0;
+                const int mask = (1 << bs_shift) - 1;
+                const int tc = min(t0 + col, t_end - 1);
+                const uint16_t *p =
+                    a.k_pool + (BIG ? gb + (int64_t)(tc & mask) * row_elems : token_offset(tc)) + 8 * grp;
 #pragma unroll
-        for (int i = 0; i < NV; i++) {
-            const int c = lane + 64 * i;
-            const int tvc = min(t0 + c / (D / 8), t_end - 1);
-            const int64_t off = BIG ? gb + (int64_t)(tvc & mask) * row_elems : token_offset(tvc);
-            vd[i] = load16(a.v_pool + off + (c % (D / 8)) * 8);
-        }
-    };
+                for (int ks = 0; ks < NKS; ks++) kd[ks] = load16(p + 32 * ks);
+#pragma unroll
+                for (int i = 0; i < NV; i++) {
+                    const int c = lane + 64 * i;
+                    const int tvc = min(t0 + c / (D / 8), t_end - 1);
+                    const int64_t off = BIG ? gb + (int64_t)(tvc & mask) * row_elems : token_offset(tvc);
+                    vd[i] = load16(a.v_pool + off + (c % (D / 8)) * 8);
+                }
+            };
+            // Fold one group of 16 tokens into the running state.
+            auto process = [&](int t0, const u32x4 *kr, const u32x4 *vr, uint16_t *vb) {
+                // stage this group's V rows in the wave's LDS (two buffers, so
+                // the next group's stores never race this group's transposed
+                // reads; LDS operations of one wave complete in order)
+#pragma unroll
+                for (int i = 0; i < NV; i++) {
+                    const int c = lane + 64 * i;
+                    *reinterpret_cast<u32x4 *>(vb + (c / (D / 8)) * VST + (c % (D / 8)) * 8) = vr[i];
+                }
+                // S^T = K Q^T (16 tokens x 16 q heads)
+                f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++)
+                    sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[ks]), qf[ks], sv, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (t0 + 4 * grp + r >= t_end) sv[r] = -INFINITY;
+                const float lmax = max3f(sv[0], sv[1], max3f(sv[2], sv[3], sv[3]));
+                if (__builtin_amdgcn_ballot_w64(lmax > m_ref + thresh || (m_ref == -INFINITY && lmax > -INFINITY))) {
+                    float mx = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    const float m_new = fmaxf(m_ref, mx);
+                    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+                    l_part *= alpha;
+#pragma unroll
+                    for (int dc = 0; dc < NDC; dc++) o[dc] *= alpha;
+                    m_ref = m_new;
+                }
+                const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * sl2;
+                const float p0 = fast_exp2(fmaf(sv[0], sl2, -mc)), p1 = fast_exp2(fmaf(sv[1], sl2, -mc));
+                const float p2 = fast_exp2(fmaf(sv[2], sl2, -mc)), p3 = fast_exp2(fmaf(sv[3], sl2, -mc));
+                const uint32_t u0 = pack_bf16x2(p0, p1), u1 = pack_bf16x2(p2, p3);
+                l_part += (p0 + p1) + (p2 + p3);
+                const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{u0, u1});
+                const uint16_t *vrow = vb + (4 * grp + ((lane & 15) >> 2)) * VST + 4 * (lane & 3);
+#pragma unroll
+                for (int dc = 0; dc < NDC; dc++) {
+                    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * dc));
+                    o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dc], 0, 0, 0);
+                }
+            };
 
-    // Fold one group of 16 tokens into the running state.
-    auto process = [&](int t0, const u32x4 *kr, const u32x4 *vr, uint16_t *vb) {
-        // stage this group's V rows in the wave's LDS (two buffers, so the
-        // next group's stores never race this group's transposed reads; LDS
-        // operations of one wave complete in order)
-#pragma unroll
-        for (int i = 0; i < NV; i++) {
-            const int c = lane + 64 * i;
-            *reinterpret_cast<u32x4 *>(vb + (c / (D / 8)) * VST + (c % (D / 8)) * 8) = vr[i];
+            // Two register sets alternate (no copies between them), so the
+            // loads of the next group are in flight while this one is processed.
+            u32x4 ka[NKS], va_[NV], kb[NKS], vb_[NV];
+            load_group(c_begin, ka, va_);
+            for (int t0 = c_begin; t0 < t_end; t0 += 2 * kGroup) {
+                if (t0 + kGroup < t_end) load_group(t0 + kGroup, kb, vb_);
+                process(t0, ka, va_, vbuf[wave][0]);
+                if (t0 + kGroup >= t_end) break;
+                if (t0 + 2 * kGroup < t_end) load_group(t0 + 2 * kGroup, ka, va_);
+                process(t0 + kGroup, kb, vb_, vbuf[wave][1]);
+            }
+            c_begin = t_end;
         }
-        // S^T = K Q^T (16 tokens x 16 q heads)
-        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ks++)
-            sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[ks]), qf[ks], sv, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-            if (t0 + 4 * grp + r >= t_end) sv[r] = -INFINITY;
-        const float lmax = max3f(sv[0], sv[1], max3f(sv[2], sv[3], sv[3]));
-        if (__builtin_amdgcn_ballot_w64(lmax > m_ref + thresh || (m_ref == -INFINITY && lmax > -INFINITY))) {
-            float mx = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_ref, mx);
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref - m_new) * sl2);
-            l_part *= alpha;
-#pragma unroll
-            for (int dc = 0; dc < NDC; dc++) o[dc] *= alpha;
-            m_ref = m_new;
-        }
-        const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * sl2;
-        const float p0 = fast_exp2(fmaf(sv[0], sl2, -mc)), p1 = fast_exp2(fmaf(sv[1], sl2, -mc));
-        const float p2 = fast_exp2(fmaf(sv[2], sl2, -mc)), p3 = fast_exp2(fmaf(sv[3], sl2, -mc));
-        const uint32_t u0 = pack_bf16x2(p0, p1), u1 = pack_bf16x2(p2, p3);
-        l_part += (p0 + p1) + (p2 + p3);
-        const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{u0, u1});
-        const uint16_t *vrow = vb + (4 * grp + ((lane & 15) >> 2)) * VST + 4 * (lane & 3);
-#pragma unroll
-        for (int dc = 0; dc < NDC; dc++) {
-            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 16 * dc));
-            o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dc], 0, 0, 0);
-        }
-    };
 
-    // Two register sets alternate (no copies between them), so the loads of
-    // the next group are in flight while this one is processed.
-    u32x4 ka[NKS], va_[NV], kb[NKS], vb_[NV];
-    load_group(t_begin, ka, va_);
-    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-        if (t0 + 16 < t_end) load_group(t0 + 16, kb, vb_);
-        process(t0, ka, va_, vbuf[wave][0]);
-        if (t0 + 16 >= t_end) break;
-        if (t0 + 32 < t_end) load_group(t0 + 32, ka, va_);
-        process(t0 + 16, kb, vb_, vbuf[wave][1]);
-    }
-    float l_run = l_part + __shfl_xor(l_part, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-
-    if (q_ok) {
-        const int64_t idx = ((int64_t)s * a.num_q_heads + qh0 + col) * a.n_splits + split;
-        if (grp == 0) {
-            a.ws_m[idx] = m_ref;
-            a.ws_l[idx] = l_run;
-        }
-        float *op = a.ws_o + idx * D + 4 * grp;
+        // this piece's partial state (unnormalised o, l, and the reference max)
+        float l_run = l_part + __shfl_xor(l_part, 16, 64);
+        l_run += __shfl_xor(l_run, 32, 64);
+        if (q_ok) {
+            const int64_t idx = ((int64_t)(blockIdx.x + s) * a.num_q_heads + qh0 + col);
+            if (grp == 0) {
+                a.ws_m[idx] = m_ref;
+                a.ws_l[idx] = l_run;
+            }
+            float *op = a.ws_o + idx * D + 4 * grp;
 #pragma unroll
-        for (int dc = 0; dc < NDC; dc++) *reinterpret_cast<f32x4 *>(op + 16 * dc) = o[dc];
+            for (int dc = 0; dc < NDC; dc++) *reinterpret_cast<f32x4 *>(op + 16 * dc) = o[dc];
+        }
     }
 }
 
-// Merge the partial states of every split of a sequence and finalize:
-// M = max m_c, L = sum l_c 2^{(m_c - M) c}, O = sum o_c 2^{(m_c - M) c},
-// out = O / L (0 when L == 0, i.e. an empty context).
+// Merge the pieces of each sequence and finalize: M = max m_c,
+// L = sum l_c 2^{(m_c - M) c}, O = sum o_c 2^{(m_c - M) c}, out = O / L
+// (0 when L == 0, i.e. an empty context).  One wave per (sequence, q head).
 template <int D>
 __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 {
@@ -219,24 +285,41 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
     if (pair >= (int64_t)a.num_seqs * a.num_q_heads) return;
-    const int s = (int)(pair / a.num_q_heads);
-    const int ctx = a.context_lens[s];
-    const int ns = ctx > 0 ? (ctx + kSplit - 1) / kSplit : 0;
-    const int64_t base = pair * a.n_splits;
+    const int s = (int)(pair / a.num_q_heads), qh = (int)(pair % a.num_q_heads);
+    const int32_t *goff = a.ws_goff;
+    const int G = goff[a.num_seqs];
+    const int P = max(1, G / a.n_ranges + (G % a.n_ranges != 0));
+    const int gs0 = goff[s], gs1 = goff[s + 1];
+    // ranges w_first..w_last hold the pieces of sequence s (none when empty);
+    // the clamp keeps the reads inside the workspace whatever goff holds
+    const int w_first = min(gs0 / P, a.n_ranges - 1);
+    const int npieces = gs1 > gs0 ? min((gs1 - 1) / P, a.n_ranges - 1) - w_first + 1 : 0;
+    auto slot = [&](int c) -> int64_t { return (int64_t)(w_first + c + s) * a.num_q_heads + qh; };
     float M = -INFINITY;
-    for (int c = lane; c < ns; c += 64) M = fmaxf(M, a.ws_m[base + c]);
+    for (int c = lane; c < npieces; c += 64) M = fmaxf(M, a.ws_m[slot(c)]);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     const float m_use = M == -INFINITY ? 0.f : M;
     float L = 0.f, acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) acc[i] = 0.f;
-    for (int c = 0; c < ns; c++) {
-        const float wgt = fast_exp2((a.ws_m[base + c] - m_use) * a.scale_log2);
-        L += a.ws_l[base + c] * wgt;
-        const float *oc = a.ws_o + (base + c) * D;
+    for (int c0 = 0; c0 < npieces; c0 += 64) {
+        // lane j holds piece c0 + j: its weight 2^{(m_c - M) c} and l_c
+        const int c = c0 + lane;
+        float wgt = 0.f;
+        if (c < npieces) {
+            wgt = fast_exp2((a.ws_m[slot(c)] - m_use) * a.scale_log2);
+            L += a.ws_l[slot(c)] * wgt;
+        }
+        const int n = min(64, npieces - c0);
+#pragma unroll 4
+        for (int j = 0; j < n; j++) {
+            const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), j));
+            const float *oc = a.ws_o + slot(c0 + j) * D + lane;
 #pragma unroll
-        for (int i = 0; i < PER; i++) acc[i] += wgt * oc[lane + 64 * i];
+            for (int i = 0; i < PER; i++) acc[i] += wj * oc[64 * i];
+        }
     }
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t *out = a.out + pair * D;
 #pragma unroll
@@ -262,28 +345,35 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(const uint16_t *pool,
     }
 }
 
-int64_t decode_n_splits(int32_t max_blocks_per_seq, int32_t block_size)
+// Ranges of token groups: enough waves for one full round on a 256-CU device
+// (256 CUs x 4 SIMDs x the split kernel's waves per SIMD: 4, 2 and 1 at
+// head_dim 64, 128 and 256), spread over the kv-head units.
+int32_t decode_n_ranges(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim)
 {
-    const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
-    return (tokens + kSplit - 1) / kSplit;
+    const int ratio = num_q_heads / num_kv_heads;
+    const int units = num_kv_heads * ((ratio + 15) / 16);
+    const int waves = 256 * 4 * (head_dim == 64 ? 4 : head_dim == 128 ? 2 : 1);
+    return max(1, waves / units);
 }
 
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t n_splits)
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim)
 {
-    const size_t n = (size_t)num_seqs * (size_t)num_q_heads * (size_t)n_splits;
-    const size_t ml = (2 * n * sizeof(float) + 255) / 256 * 256;
-    return ml + n * (size_t)head_dim * sizeof(float);
+    const size_t goff = ((size_t)num_seqs + 1) * sizeof(int32_t);
+    const size_t slots = (size_t)decode_n_ranges(num_q_heads, num_kv_heads, head_dim) + (size_t)num_seqs;
+    const size_t n = slots * (size_t)num_q_heads;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return up(goff) + up(2 * n * sizeof(float)) + n * (size_t)head_dim * sizeof(float);
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
 {
+    hipLaunchKernelGGL(paged_decode_offsets_kernel, dim3(1), dim3(256), 0, stream, a.context_lens, a.num_seqs,
+                       a.max_blocks, a.bs_shift, a.ws_goff);
     const int64_t units = (int64_t)a.num_kv_heads * a.n_sub;
-    if (a.n_splits > 0) {
-        const dim3 grid((unsigned)((int64_t)a.num_seqs * a.n_splits), (unsigned)((units + 3) / 4)), block(256);
-        if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, block, 0, stream, a);
-    }
+    const dim3 grid((unsigned)a.n_ranges, (unsigned)((units + 3) / 4)), block(256);
+    if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, block, 0, stream, a);
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
     hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();

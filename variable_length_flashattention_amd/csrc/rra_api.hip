@@ -106,11 +106,12 @@ int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, in
     return hip_status(e);
 }
 
-size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                        int32_t max_blocks_per_seq, int32_t block_size)
+size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim)
 {
-    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq < 0 || block_size <= 0) return 0;
-    return decode_workspace_bytes(num_seqs, num_q_heads, head_dim, decode_n_splits(max_blocks_per_seq, block_size));
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+    if (!supported_head_dim(head_dim)) return 0;
+    return decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
 }
 
 static int32_t log2_exact(int32_t x)
@@ -138,8 +139,7 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
     if (num_seqs == 0) return RRA_OK;
     if (!q || !out || !block_table || !context_lens) return RRA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return RRA_ERR_INVALID_ARG;
-    const int64_t n_splits = decode_n_splits(max_blocks_per_seq, block_size);
-    const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n_splits);
+    const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RRA_ERR_WORKSPACE;
 
     DecodeArgs a;
@@ -149,18 +149,25 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
     a.block_table = block_table;
     a.context_lens = context_lens;
     a.out = static_cast<uint16_t *>(out);
-    const size_t n = (size_t)num_seqs * num_q_heads * n_splits;
+    // workspace: goff [num_seqs + 1] int32 | m, l [slots * num_q_heads] fp32 |
+    // o [slots * num_q_heads * head_dim] fp32, slots = n_ranges + num_seqs,
+    // each part starting on a 256-byte boundary
+    const int32_t n_ranges = decode_n_ranges(num_q_heads, num_kv_heads, head_dim);
+    const size_t n = ((size_t)n_ranges + (size_t)num_seqs) * num_q_heads;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     char *ws = static_cast<char *>(workspace);
+    a.ws_goff = reinterpret_cast<int32_t *>(ws);
+    ws += up(((size_t)num_seqs + 1) * sizeof(int32_t));
     a.ws_m = reinterpret_cast<float *>(ws);
     a.ws_l = a.ws_m + n;
-    a.ws_o = reinterpret_cast<float *>(ws + (2 * n * sizeof(float) + 255) / 256 * 256);
+    a.ws_o = reinterpret_cast<float *>(ws + up(2 * n * sizeof(float)));
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.bs_shift = bs_shift;
     a.max_blocks = max_blocks_per_seq;
-    a.n_splits = (int32_t)n_splits;
+    a.n_ranges = n_ranges;
     const int32_t ratio = num_q_heads / num_kv_heads;
     a.n_sub = (ratio + 15) / 16;
     a.scale_log2 = softmax_scale * kLog2e;

@@ -20,9 +20,6 @@ inline int varlen_block_q(int head_dim, int max_seqlen_q)
 // for about 1700 sequences; more fall back to decoding from global memory).
 constexpr int kSchedInts = 3584;
 
-// Tokens per split of the paged decode.
-constexpr int kDecodeSplitTokens = 256;
-
 struct VarlenArgs {
     const uint16_t *q, *k, *v;
     uint16_t *out;
@@ -45,16 +42,17 @@ struct DecodeArgs {
     const uint16_t *q, *k_pool, *v_pool;
     const int32_t *block_table, *context_lens;
     uint16_t *out;
-    float *ws_m, *ws_l, *ws_o;
+    int32_t *ws_goff;    // [num_seqs + 1] token-group offsets of the sequences
+    float *ws_m, *ws_l, *ws_o;  // [n_ranges + num_seqs] x num_q_heads partial states
     int32_t num_seqs, num_q_heads, num_kv_heads;
     int32_t block_size, bs_shift, max_blocks;
-    int32_t n_splits;    // splits per sequence allocated in the workspace
+    int32_t n_ranges;    // equal ranges of token groups, one wave each per kv head
     int32_t n_sub;       // q-head subgroups of 16 per kv head
     float scale_log2;
 };
 
-int64_t decode_n_splits(int32_t max_blocks_per_seq, int32_t block_size);
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t n_splits);
+int32_t decode_n_ranges(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 hipError_t launch_paged_decode(const DecodeArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_paged_gather(const uint16_t *pool, const int32_t *block_table, const int32_t *context_lens,
                                uint16_t *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,

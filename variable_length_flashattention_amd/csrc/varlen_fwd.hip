@@ -149,16 +149,15 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         if (NBUF > 3 && nkt > 2) stage(2, k_lds2, v_lds2);
 
         // Q^T operand: lane holds Q[my_i][16*ks + 8*(lane/32) .. +7]
+        // (rows past the sequence end read its last row; their results are
+        // never stored, and an unconditional load is not waited on at once)
         bf16x8 qf[RPW][NKS];
 #pragma unroll
         for (int u = 0; u < RPW; u++) {
-            const uint16_t *qrow = a.q + ((int64_t)(q0 + my_i[u]) * H + h) * D + 8 * (lane >> 5);
+            const int qr = min(my_i[u], Lq - 1);
+            const uint16_t *qrow = a.q + ((int64_t)(q0 + qr) * H + h) * D + 8 * (lane >> 5);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (row_ok[u]) x = load16(qrow + 16 * ks);
-                qf[u][ks] = as_bf16x8(x);
-            }
+            for (int ks = 0; ks < NKS; ks++) qf[u][ks] = as_bf16x8(load16(qrow + 16 * ks));
         }
         f32x16 o[RPW][NDC];
 #pragma unroll
