@@ -39,6 +39,13 @@ def build(out: str | None = None, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # A kernel body the host pass cannot handle makes it drop the kernel's
+    # launch stub without a diagnostic; the library would then fail to load.
+    r = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the host objects: " + ", ".join(missing))
     os.replace(tmp, out)
     return out
 

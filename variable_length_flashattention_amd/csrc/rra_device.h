@@ -43,6 +43,19 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __builtin_bi
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer descriptor over `base` (byte addressing, no stride, 2^31-1 bytes
+// in range; the data-format field is the one the CDNA buffer loads expect).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+// 16 bytes per lane from buffer `r` at byte offset voff + soff straight into
+// LDS: lane l writes lds + 16*l (lds is wave-uniform).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, int32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
 // max of three floats in one instruction.  Operands are finite or -inf here,
 // so the NaN canonicalisation the compiler would add around fmaxf is not needed.
 __device__ __forceinline__ float max3f(float a, float b, float c)

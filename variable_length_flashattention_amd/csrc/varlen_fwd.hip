@@ -71,7 +71,7 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
 
     __shared__ int sched[kSchedInts];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.num_heads;
     const float sl2 = a.scale_log2;
     const WorkTables wt = build_work_tables(a.cu_q, a.cu_k, a.batch, BQ, a.levels, sched, kSchedInts);
@@ -84,9 +84,14 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         if (!decode_work_item(wt, a.cu_q, H, w, lane, b, qt, h)) break;  // the same in every wave
         __syncthreads();  // LDS buffers of the previous item no longer in use
 
+        // (the item's indices are the same in every lane; saying so keeps the
+        // per-item arithmetic and the buffer descriptors scalar)
+        b = __builtin_amdgcn_readfirstlane(b);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+        h = __builtin_amdgcn_readfirstlane(h);
         const int *cuq = wt.cached ? wt.cuq : a.cu_q, *cuk = wt.cached ? wt.cuk : a.cu_k;
-        const int q0 = cuq[b], k0 = cuk[b];
-        const int Lq = cuq[b + 1] - q0, Lk = cuk[b + 1] - k0;
+        const int q0 = __builtin_amdgcn_readfirstlane(cuq[b]), k0 = __builtin_amdgcn_readfirstlane(cuk[b]);
+        const int Lq = __builtin_amdgcn_readfirstlane(cuq[b + 1]) - q0, Lk = __builtin_amdgcn_readfirstlane(cuk[b + 1]) - k0;
         const int diag = Lk - Lq;  // causal: key j visible to query i iff j <= i + diag
         const int i0 = qt * BQ;
         const int nrows = min(BQ, Lq - i0);
@@ -109,39 +114,48 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             nkt_u[u] = (kend_u + BK - 1) / BK;
         }
 
-        // Direct-to-LDS staging of key tile kt.  Wave w fills 1 KiB blocks
-        // w, w+NW, ... of each tensor; lane l of a block writes the 16 bytes at
-        // block*1024 + 16*l, i.e. row r, physical chunk p, which holds logical
-        // chunk p ^ swz(r).  Rows past the sequence end re-read its last row
-        // (their scores are masked and their probabilities are exactly 0).
-        // The per-lane source offsets of tile 0 are computed once; tile kt adds
-        // kt*BK rows, except the sequence's last tile, which clamps its rows.
+        // Direct-to-LDS staging of key tile kt with buffer loads: the tile's
+        // first row is the buffer base (64-bit, scalar), each load adds a
+        // uniform row offset (scalar) to a per-lane offset (vector) that does
+        // not change from tile to tile, so a tile costs no vector address
+        // arithmetic.  Wave w fills 1 KiB blocks w, w+NW, ... of each tensor;
+        // lane l of a block writes the 16 bytes at block*1024 + 16*l, i.e. row
+        // r, physical chunk p, which holds logical chunk p ^ swz(r).  In the
+        // sequence's last tile, rows past its end re-read its last row (their
+        // scores are masked and their probabilities are exactly 0).
         constexpr int WL = T::WAVE_LOADS;
-        int64_t koff0[WL], voff0[WL];
-        int srow[WL];
+        constexpr int RPL = NW * 1024 / ROWB;        // rows between a lane's loads
+        constexpr int NKO = RPL % 16 == 0 ? 1 : 16 / RPL;  // distinct K swizzles over the loads
+        static_assert(RPL % 4 == 0 && (RPL % 16 == 0 || 16 % RPL == 0), "swizzle period");
+        const int srow0 = (wave * 1024 + lane * 16) / ROWB, pch = (lane * 16 % ROWB) / 16;
+        const int row_bytes = H * D * 2;              // bytes from one token to the next
+        uint32_t lane_k[NKO];
 #pragma unroll
-        for (int i = 0; i < WL; i++) {
-            const int byte = (i * NW + wave) * 1024 + lane * 16;
-            const int row = byte / ROWB, pch = (byte % ROWB) / 16;
-            srow[i] = row;
-            const int64_t off = ((int64_t)(k0 + row) * H + h) * D;
-            koff0[i] = off + 8 * (pch ^ T::swz_k(row));
-            voff0[i] = off + 8 * (pch ^ T::swz_v(row));
-        }
-        const int64_t row_step = (int64_t)H * D;  // elements from one token to the next
+        for (int j = 0; j < NKO; j++)
+            lane_k[j] = (uint32_t)(srow0 * row_bytes + 16 * (pch ^ T::swz_k(srow0 + j * RPL)));
+        const uint32_t lane_v = (uint32_t)(srow0 * row_bytes + 16 * (pch ^ T::swz_v(srow0)));
+        const uint8_t *kseq = reinterpret_cast<const uint8_t *>(a.k + ((int64_t)k0 * H + h) * D);
+        const uint8_t *vseq = reinterpret_cast<const uint8_t *>(a.v + ((int64_t)k0 * H + h) * D);
         auto stage = [&](int kt, uint8_t *kb, uint8_t *vb) {
-            const bool tail = (kt + 1) * BK > Lk;
+            const int64_t toff = (int64_t)kt * BK * row_bytes;
+            const __amdgpu_buffer_rsrc_t kr = raw_buffer(kseq + toff), vr = raw_buffer(vseq + toff);
+            if ((kt + 1) * BK <= Lk) {
 #pragma unroll
-            for (int i = 0; i < WL; i++) {
-                const int blk = i * NW + wave;
-                const int rows = tail ? min(kt * BK + srow[i], Lk - 1) - srow[i] : kt * BK;
-                // (the sources go through named locals: with the address
-                // expression inline as the builtin's argument, the host pass
-                // silently dropped the kernel's launch stub)
-                const uint16_t *ksrc = a.k + koff0[i] + rows * row_step;
-                const uint16_t *vsrc = a.v + voff0[i] + rows * row_step;
-                __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void *)(kb + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void *)(vb + blk * 1024), 16, 0, 0);
+                for (int i = 0; i < WL; i++) {
+                    const int blk = i * NW + wave;
+                    buffer_to_lds16(kr, kb + blk * 1024, lane_k[i % NKO], i * RPL * row_bytes);
+                    buffer_to_lds16(vr, vb + blk * 1024, lane_v, i * RPL * row_bytes);
+                }
+            } else {
+                const int last_row = Lk - 1 - kt * BK;
+#pragma unroll
+                for (int i = 0; i < WL; i++) {
+                    const int blk = i * NW + wave;
+                    const int row = srow0 + i * RPL;
+                    const uint32_t back = (uint32_t)((row - min(row, last_row)) * row_bytes);
+                    buffer_to_lds16(kr, kb + blk * 1024, lane_k[i % NKO] - back, i * RPL * row_bytes);
+                    buffer_to_lds16(vr, vb + blk * 1024, lane_v - back, i * RPL * row_bytes);
+                }
             }
         };
         if (nkt > 0) stage(0, k_lds0, v_lds0);
@@ -206,18 +220,30 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                 for (int c = 0; c < NC; c++)
 #pragma unroll
                     for (int r = 0; r < 16; r++) s[u][c][r] = 0.f;
+            // K fragments are read KD MMAs ahead of use; the scheduling
+            // barriers keep the compiler from sinking the reads next to
+            // their MMAs (it does that under register pressure, and each
+            // MMA then waits out a full LDS latency)
+            {
+                constexpr int NM = NC * NKS, KD = 3;
+                auto kread = [&](int m) -> bf16x8 {
+                    const int c = m / NKS, ks = m % NKS;
+                    const int row = 32 * c + (lane & 31);
+                    const int ch = (2 * ks + (lane >> 5)) ^ T::swz_k(row);
+                    return as_bf16x8(*reinterpret_cast<const u32x4 *>(Kb + row * ROWB + 16 * ch));
+                };
+                bf16x8 kf[KD];
 #pragma unroll
-            for (int c = 0; c < NC; c++) {
-                const int row = 32 * c + (lane & 31);
-                const uint8_t *kp = Kb + row * ROWB;
-                const int sw = T::swz_k(row);
+                for (int m = 0; m < KD; m++) kf[m] = kread(m);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ks++) {
-                    const int ch = (2 * ks + (lane >> 5)) ^ sw;
-                    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * ch));
+                for (int m = 0; m < NM; m++) {
+                    const bf16x8 ka = kf[m % KD];
+                    if (m + KD < NM) kf[m % KD] = kread(m + KD);
+                    const int c = m / NKS, ks = m % NKS;
 #pragma unroll
                     for (int u = 0; u < RPW; u++)
                         if (act[u]) s[u][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[u][ks], s[u][c], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             uint32_t pk[RPW][NC][8];
@@ -270,28 +296,37 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
 
             // O^T += V^T P^T, 16 keys per MMA; each V operand read feeds every
             // active row block
+            // V^T fragments (two transposed reads each) one MMA ahead of use
             const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-            for (int m = 0; m < BK / 16; m++) {
-                u32x4 pb[RPW];
-#pragma unroll
-                for (int u = 0; u < RPW; u++)
-                    pb[u] = u32x4{pk[u][m >> 1][4 * (m & 1) + 0], pk[u][m >> 1][4 * (m & 1) + 1],
-                                  pk[u][m >> 1][4 * (m & 1) + 2], pk[u][m >> 1][4 * (m & 1) + 3]};
-                const int row = 16 * m + 4 * (g >> 1) + (j >> 2);
-                const int sw = T::swz_v(row);  // rows row and row+8 share it
-                const uint8_t *v0 = Vb + row * ROWB + 8 * (j & 1);
-#pragma unroll
-                for (int dc = 0; dc < NDC; dc++) {
+            {
+                constexpr int NM = (BK / 16) * NDC, VD = 2;
+                auto vread = [&](int mm) -> u32x4 {
+                    const int m = mm / NDC, dc = mm % NDC;
+                    const int row = 16 * m + 4 * (g >> 1) + (j >> 2);
+                    const int sw = T::swz_v(row);  // rows row and row+8 share it
+                    const uint8_t *v0 = Vb + row * ROWB + 8 * (j & 1);
                     const int ch = (4 * dc + 2 * (g & 1) + ((j & 3) >> 1)) ^ sw;
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 16 * ch));
                     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(v0 + 8 * ROWB + 16 * ch));
-                    const u32x4 vv = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+                    return u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                 __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+                };
+                u32x4 vf[VD];
 #pragma unroll
-                    for (int u = 0; u < RPW; u++)
+                for (int mm = 0; mm < VD; mm++) vf[mm] = vread(mm);
+#pragma unroll
+                for (int mm = 0; mm < NM; mm++) {
+                    const u32x4 vv = vf[mm % VD];
+                    if (mm + VD < NM) vf[mm % VD] = vread(mm + VD);
+                    const int m = mm / NDC, dc = mm % NDC;
+#pragma unroll
+                    for (int u = 0; u < RPW; u++) {
+                        const u32x4 pb = {pk[u][m >> 1][4 * (m & 1) + 0], pk[u][m >> 1][4 * (m & 1) + 1],
+                                          pk[u][m >> 1][4 * (m & 1) + 2], pk[u][m >> 1][4 * (m & 1) + 3]};
                         if (act[u])
-                            o[u][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb[u]), o[u][dc], 0, 0, 0);
+                            o[u][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), o[u][dc], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
