@@ -58,6 +58,11 @@ CASES = [
     ("bs1_multi_chunk", [20000, 3], 1024, 1, 64, 1),             # 320 tokens per range
     ("bs16_multi_chunk", [36000, 100, 0], 2048, 1, 64, 16),      # 1136 tokens per range
     ("d256_ranges", [3000, 1, 4500], 64, 4, 256, 32),
+    # up to 256 sequences each wave derives the group offsets itself; above,
+    # they come from the offsets kernel through a 64-way search
+    ("seqs_256", np.random.Generator(np.random.PCG64(78)).integers(0, 300, 256).tolist(), 8, 2, 128, 16),
+    ("seqs_257", np.random.Generator(np.random.PCG64(79)).integers(0, 300, 257).tolist(), 8, 2, 128, 16),
+    ("seqs_5000", np.random.Generator(np.random.PCG64(80)).integers(0, 40, 5000).tolist(), 4, 4, 64, 8),
 ]
 
 

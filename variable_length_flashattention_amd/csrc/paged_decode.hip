@@ -79,17 +79,90 @@ __global__ __launch_bounds__(256) void paged_decode_offsets_kernel(const int32_t
     if (tid == 0) goff[num_seqs] = carry;
 }
 
-// first s in [0, S) with goff[s + 1] > g (g < goff[S])
-__device__ __forceinline__ int seq_of_group(const int32_t *__restrict__ goff, int S, int g)
-{
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (goff[mid + 1] > g) hi = mid;
-        else lo = mid + 1;
+// Token-group offsets goff(s), s = 0..S, and context lengths as one wave
+// sees them.  Up to kRegSeqs sequences the wave computes them itself from
+// context_lens into registers (lane j holds goff(64 i + j + 1) and the
+// clamped ctx of sequence 64 i + j in register i), so no offsets kernel runs
+// and no lookup waits on memory; larger batches read the offsets the offsets
+// kernel wrote and search them 64 ways per round trip.  All queries take a
+// wave-uniform argument and return a wave-uniform value.
+constexpr int kRegSeqs = 256;
+struct GroupOffsets {
+    int incl[kRegSeqs / 64], ctxr[kRegSeqs / 64];
+    const int32_t *mem;
+    const int32_t *ctx_mem;
+    int S, max_blocks, bs_shift;
+    bool in_regs;
+
+    __device__ __forceinline__ void init(const int32_t *context_lens, const int32_t *goff_mem, int num_seqs,
+                                         int max_blocks_, int bs_shift_, int lane)
+    {
+        S = num_seqs;
+        mem = goff_mem;
+        ctx_mem = context_lens;
+        max_blocks = max_blocks_;
+        bs_shift = bs_shift_;
+        in_regs = S <= kRegSeqs;
+        if (!in_regs) return;
+        int raw[kRegSeqs / 64];
+#pragma unroll
+        for (int i = 0; i < kRegSeqs / 64; i++) {
+            const int s = 64 * i + lane;
+            raw[i] = (64 * i < S && s < S) ? context_lens[s] : 0;
+        }
+        int carry = 0;
+#pragma unroll
+        for (int i = 0; i < kRegSeqs / 64; i++) {
+            ctxr[i] = clamp_ctx(raw[i], max_blocks, bs_shift);
+            const int g = (ctxr[i] + kGroup - 1) / kGroup;
+            int x = g;  // inclusive scan within the wave
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            incl[i] = x + carry;
+            carry = __builtin_amdgcn_readlane(incl[i], 63);
+        }
     }
-    return lo;
-}
+    // register i's value in lane j (i, j wave-uniform)
+    __device__ __forceinline__ static int pick(const int *r, int i, int j)
+    {
+        const int v = i == 0 ? r[0] : i == 1 ? r[1] : i == 2 ? r[2] : r[3];
+        return __builtin_amdgcn_readlane(v, j);
+    }
+    __device__ __forceinline__ int goff(int s) const
+    {
+        if (!in_regs) return mem[s];
+        return s == 0 ? 0 : pick(incl, (s - 1) >> 6, (s - 1) & 63);
+    }
+    __device__ __forceinline__ int ctx(int s) const
+    {
+        return in_regs ? pick(ctxr, s >> 6, s & 63) : clamp_ctx(ctx_mem[s], max_blocks, bs_shift);
+    }
+    // first s in [0, S) with goff(s + 1) > g, for 0 <= g < goff(S)
+    __device__ __forceinline__ int seq_of_group(int g, int lane) const
+    {
+        if (in_regs) {
+#pragma unroll
+            for (int i = 0; i < kRegSeqs / 64; i++) {
+                const uint64_t m = __ballot(64 * i + lane < S && incl[i] > g);
+                if (m) return 64 * i + __ffsll((unsigned long long)m) - 1;
+            }
+            return S - 1;  // not reached
+        }
+        int lo = 0, hi = S - 1;  // the answer is in [lo, hi]
+        while (lo < hi) {
+            const int step = (hi - lo + 62) / 63;  // lane 63 samples hi
+            const int idx = min(hi, lo + lane * step);
+            const uint64_t m = __ballot(mem[idx + 1] > g);  // true at idx = hi
+            const int f = __ffsll((unsigned long long)m) - 1;
+            const int idx_f = min(hi, lo + f * step);
+            lo = f == 0 ? lo : lo + (f - 1) * step + 1;
+            hi = idx_f;
+        }
+        return lo;
+    }
+};
 
 // BIG: block_size >= 16, so each group of 16 tokens sits in one pool block
 // and its block id is wave-uniform.
@@ -108,8 +181,9 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     if (unit >= a.num_kv_heads * a.n_sub) return;  // no block-level barriers below
     const int kh = unit / a.n_sub, sub = unit % a.n_sub;
     const int S = a.num_seqs;
-    const int32_t *goff = a.ws_goff;
-    const int G = goff[S];
+    GroupOffsets go;
+    go.init(a.context_lens, a.ws_goff, S, a.max_blocks, a.bs_shift, lane);
+    const int G = go.goff(S);
     const int P = G / a.n_ranges + (G % a.n_ranges != 0);  // groups per range
     const int64_t g_lo64 = (int64_t)blockIdx.x * P;
     if (g_lo64 >= G) return;
@@ -127,11 +201,12 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     const float thresh = 8.f / sl2;                // raw-score headroom above the reference max
     const int64_t row_elems = (int64_t)Hkv * D;    // elements per pool token row
 
-    for (int s = seq_of_group(goff, S, g_lo); s < S && goff[s] < g_hi; s++) {
-        const int gs0 = goff[s];
-        const int ctx = clamp_ctx(a.context_lens[s], a.max_blocks, bs_shift);
+    for (int s = go.seq_of_group(g_lo, lane), gs0 = go.goff(s); s < S && gs0 < g_hi; s++) {
+        const int gs1 = go.goff(s + 1);
+        const int ctx = go.ctx(s);
         const int seg_begin = kGroup * (max(g_lo, gs0) - gs0);
-        const int seg_end = min(ctx, kGroup * (min(g_hi, goff[s + 1]) - gs0));
+        const int seg_end = min(ctx, kGroup * (min(g_hi, gs1) - gs0));
+        gs0 = gs1;  // the next sequence's first group
         if (seg_begin >= seg_end) continue;
         const int32_t *bt = a.block_table + (int64_t)s * a.max_blocks;
 
@@ -277,21 +352,32 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
 
 // Merge the pieces of each sequence and finalize: M = max m_c,
 // L = sum l_c 2^{(m_c - M) c}, O = sum o_c 2^{(m_c - M) c}, out = O / L
-// (0 when L == 0, i.e. an empty context).  One wave per (sequence, q head).
+// (0 when L == 0, i.e. an empty context).  One workgroup of NWC waves per
+// (sequence, q head): every wave finds M and L over all pieces (lane-parallel
+// loads), the waves split the o sums, and wave 0 adds their partial sums
+// from LDS.  A piece's o is D floats; LP = D/4 lanes read it as 16-byte
+// pieces, so one wave load covers 64/LP pieces, each lane weighting its own
+// piece (weights are held one piece per lane and fetched with a lane
+// shuffle).
+constexpr int kCombineWaves = 4;
 template <int D>
-__global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kernel(DecodeArgs a)
 {
-    constexpr int PER = D / 64;
+    constexpr int NWC = kCombineWaves;
+    constexpr int LP = D / 4 < 64 ? D / 4 : 64;   // lanes per piece
+    constexpr int PPL = 64 / LP;                   // pieces per wave load
+    constexpr int NA = D / LP / 4;                 // 16-byte pieces per lane
+    __shared__ __attribute__((aligned(16))) float part[NWC - 1][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
-    if (pair >= (int64_t)a.num_seqs * a.num_q_heads) return;
+    const int64_t pair = blockIdx.x;
     const int s = (int)(pair / a.num_q_heads), qh = (int)(pair % a.num_q_heads);
-    const int32_t *goff = a.ws_goff;
-    const int G = goff[a.num_seqs];
+    GroupOffsets go;
+    go.init(a.context_lens, a.ws_goff, a.num_seqs, a.max_blocks, a.bs_shift, lane);
+    const int G = go.goff(a.num_seqs);
     const int P = max(1, G / a.n_ranges + (G % a.n_ranges != 0));
-    const int gs0 = goff[s], gs1 = goff[s + 1];
+    const int gs0 = go.goff(s), gs1 = go.goff(s + 1);
     // ranges w_first..w_last hold the pieces of sequence s (none when empty);
-    // the clamp keeps the reads inside the workspace whatever goff holds
+    // the clamp keeps the reads inside the workspace whatever the offsets hold
     const int w_first = min(gs0 / P, a.n_ranges - 1);
     const int npieces = gs1 > gs0 ? min((gs1 - 1) / P, a.n_ranges - 1) - w_first + 1 : 0;
     auto slot = [&](int c) -> int64_t { return (int64_t)(w_first + c + s) * a.num_q_heads + qh; };
@@ -299,11 +385,13 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
     for (int c = lane; c < npieces; c += 64) M = fmaxf(M, a.ws_m[slot(c)]);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     const float m_use = M == -INFINITY ? 0.f : M;
-    float L = 0.f, acc[PER];
+    float L = 0.f;
+    f32x4 acc[NA];
 #pragma unroll
-    for (int i = 0; i < PER; i++) acc[i] = 0.f;
+    for (int i = 0; i < NA; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int sub = lane / LP, dl = lane % LP;  // this lane's piece within a load, and d chunk
     for (int c0 = 0; c0 < npieces; c0 += 64) {
-        // lane j holds piece c0 + j: its weight 2^{(m_c - M) c} and l_c
+        // lane j holds piece c0 + j: its weight 2^{(m_c - M) c} (0 past the end)
         const int c = c0 + lane;
         float wgt = 0.f;
         if (c < npieces) {
@@ -311,19 +399,46 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
             L += a.ws_l[slot(c)] * wgt;
         }
         const int n = min(64, npieces - c0);
+        // this wave's loads: pieces wave*PPL + k*NWC*PPL (+ sub) of the chunk
 #pragma unroll 4
-        for (int j = 0; j < n; j++) {
-            const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), j));
-            const float *oc = a.ws_o + slot(c0 + j) * D + lane;
+        for (int j = wave * PPL; j < n; j += NWC * PPL) {
+            const int jj = j + sub;  // this lane's piece, relative to c0
+            const float wj = __shfl(wgt, jj & 63, 64);
+            const int cc = min(c0 + jj, npieces - 1);  // (weight 0 past the end)
+            const float *oc = a.ws_o + slot(cc) * D + 4 * dl;
 #pragma unroll
-            for (int i = 0; i < PER; i++) acc[i] += wj * oc[64 * i];
+            for (int i = 0; i < NA; i++) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(oc + 4 * LP * i);
+                acc[i] += (jj < n ? wj : 0.f) * v;
+            }
         }
     }
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint16_t *out = a.out + pair * D;
+    // lanes l and l + k*LP hold the same d range for different pieces
 #pragma unroll
-    for (int i = 0; i < PER; i++) out[lane + 64 * i] = (uint16_t)(pack_bf16x2(acc[i] * inv, 0.f) & 0xffffu);
+    for (int off = LP; off < 64; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < NA; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[i][e] += __shfl_xor(acc[i][e], off, 64);
+    if (wave > 0 && sub == 0) {
+#pragma unroll
+        for (int i = 0; i < NA; i++) *reinterpret_cast<f32x4 *>(&part[wave - 1][4 * dl + 4 * LP * i]) = acc[i];
+    }
+    __syncthreads();
+    if (wave == 0 && sub == 0) {
+#pragma unroll
+        for (int w = 0; w < NWC - 1; w++)
+#pragma unroll
+            for (int i = 0; i < NA; i++) acc[i] += *reinterpret_cast<const f32x4 *>(&part[w][4 * dl + 4 * LP * i]);
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        uint16_t *out = a.out + pair * D + 4 * dl;
+#pragma unroll
+        for (int i = 0; i < NA; i++) {
+            const u32x2 pr = {pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv), pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv)};
+            *reinterpret_cast<u32x2 *>(out + 4 * LP * i) = pr;
+        }
+    }
 }
 
 // Test hook: the split kernel's address computation, as a plain copy.
@@ -368,14 +483,15 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(paged_decode_offsets_kernel, dim3(1), dim3(256), 0, stream, a.context_lens, a.num_seqs,
-                       a.max_blocks, a.bs_shift, a.ws_goff);
+    if (a.num_seqs > kRegSeqs)
+        hipLaunchKernelGGL(paged_decode_offsets_kernel, dim3(1), dim3(256), 0, stream, a.context_lens, a.num_seqs,
+                           a.max_blocks, a.bs_shift, a.ws_goff);
     const int64_t units = (int64_t)a.num_kv_heads * a.n_sub;
     const dim3 grid((unsigned)a.n_ranges, (unsigned)((units + 3) / 4)), block(256);
     if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, block, 0, stream, a);
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
-    hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)pairs), dim3(64 * kCombineWaves), 0, stream, a);
     return hipGetLastError();
 }
 

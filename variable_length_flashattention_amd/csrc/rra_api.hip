@@ -136,6 +136,7 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
     const int32_t bs_shift = log2_exact(block_size);
     if (bs_shift < 0 || block_size > 1024) return RRA_ERR_UNSUPPORTED;
     if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return RRA_ERR_INVALID_ARG;
+    if ((int64_t)num_seqs * num_q_heads > INT32_MAX) return RRA_ERR_INVALID_ARG;  // one combine workgroup each
     if (num_seqs == 0) return RRA_OK;
     if (!q || !out || !block_table || !context_lens) return RRA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return RRA_ERR_INVALID_ARG;
