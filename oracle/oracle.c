@@ -100,9 +100,12 @@ static int run_units(unit_fn fn, void *ctx, int64_t n_units, size_t scratch_len,
 /* Variable-length attention forward.                                       */
 /*                                                                          */
 /* Layout ([PLAN] Task 1 preconditions; Task 2 "Layout"): q, out are        */
-/* [total_q, H, D], k, v are [total_k, H, D], element (t, h, d) at          */
+/* [total_q, H, D], k, v are [total_k, Hkv, D], element (t, h, d) at        */
 /* (t*H + h)*D + d.  lse is [total_q, H].  Sequence b owns the half-open    */
-/* token ranges [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]).              */
+/* token ranges [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]).  Query head  */
+/* h reads kv head h / (H / Hkv): contiguous groups, the grouping of the    */
+/* decode page ([DECODE] step_tile_ref); Hkv == H is plain multi-head       */
+/* attention as in [PLAN].                                                  */
 /*                                                                          */
 /* For query i of sequence b and head h, with A(i) the visible keys:        */
 /*   s_j = scale * sum_d q[i,d] k[j,d]                 (j in A(i))          */
@@ -120,6 +123,7 @@ typedef struct {
     double *out, *lse;
     /* sampled-row mode */
     const int32_t *rows; /* pairs (token, head) */
+    int32_t Hkv;         /* kv heads; H % Hkv == 0 */
 } varlen_ctx;
 
 /* Is key j visible to query i?  Bottom-right causal alignment. */
@@ -134,7 +138,8 @@ static int key_visible(int64_t i, int64_t j, int64_t Lq, int64_t Lk, int causal)
 static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
                        double *scratch, double *out_row, double *lse_out)
 {
-    const int64_t H = c->H, D = c->D;
+    const int64_t H = c->H, D = c->D, Hkv = c->Hkv;
+    const int64_t kh = h / (H / Hkv);
     const int64_t q0 = c->cu_q[b], k0 = c->cu_k[b];
     const int64_t Lq = (int64_t)c->cu_q[b + 1] - q0;
     const int64_t Lk = (int64_t)c->cu_k[b + 1] - k0;
@@ -145,7 +150,7 @@ static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
     int64_t n_visible = 0;
     for (int64_t j = 0; j < Lk; j++) {
         if (!key_visible(i, j, Lq, Lk, c->causal)) { scratch[j] = -INFINITY; continue; }
-        const uint16_t *krow = c->k + ((k0 + j) * H + h) * D;
+        const uint16_t *krow = c->k + ((k0 + j) * Hkv + kh) * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(krow[d]);
         scratch[j] = c->scale * dot;
@@ -166,7 +171,7 @@ static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
     for (int64_t j = 0; j < Lk; j++) {
         if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
         const double w = exp(scratch[j] - M) / Z;
-        const uint16_t *vrow = c->v + ((k0 + j) * H + h) * D;
+        const uint16_t *vrow = c->v + ((k0 + j) * Hkv + kh) * D;
         for (int64_t d = 0; d < D; d++) out_row[d] += w * bf16_value(vrow[d]);
     }
     *lse_out = M + log(Z);
@@ -196,16 +201,26 @@ static int64_t max_len(const int32_t *cu, int32_t batch)
 }
 
 /* Returns 0 on success, -1 on bad arguments or allocation failure. */
+int oracle_varlen_attn_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, double scale,
+                           int32_t causal, double *out, double *lse, int32_t nthreads)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0) return -1;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
+    for (int32_t b = 0; b < batch; b++)
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
+    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, NULL, num_kv_heads};
+    return run_units(varlen_unit, &c, (int64_t)batch * num_heads, (size_t)max_len(cu_k, batch), nthreads);
+}
+
 int oracle_varlen_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
                        int32_t num_heads, int32_t head_dim, double scale, int32_t causal,
                        double *out, double *lse, int32_t nthreads)
 {
-    if (batch < 0 || num_heads <= 0 || head_dim <= 0) return -1;
-    for (int32_t b = 0; b < batch; b++)
-        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
-    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, NULL};
-    return run_units(varlen_unit, &c, (int64_t)batch * num_heads, (size_t)max_len(cu_k, batch), nthreads);
+    return oracle_varlen_attn_gqa(q, k, v, cu_q, cu_k, batch, num_heads, num_heads, head_dim, scale, causal,
+                                  out, lse, nthreads);
 }
 
 /* Sampled rows: rows[2r] = packed query token, rows[2r+1] = head.  Writes
@@ -220,19 +235,30 @@ static void varlen_sample_unit(void *p, int64_t r, double *scratch)
     varlen_row(c, b, (int64_t)t - c->cu_q[b], h, scratch, c->out + r * c->D, c->lse + r);
 }
 
+int oracle_varlen_attn_rows_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, double scale,
+                                int32_t causal, const int32_t *rows, int64_t n_rows,
+                                double *out, double *lse, int32_t nthreads)
+{
+    if (batch <= 0 || num_heads <= 0 || head_dim <= 0) return -1;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
+    for (int64_t r = 0; r < n_rows; r++) {
+        if (rows[2 * r] < cu_q[0] || rows[2 * r] >= cu_q[batch]) return -1;
+        if (rows[2 * r + 1] < 0 || rows[2 * r + 1] >= num_heads) return -1;
+    }
+    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, rows, num_kv_heads};
+    return run_units(varlen_sample_unit, &c, n_rows, (size_t)max_len(cu_k, batch), nthreads);
+}
+
 int oracle_varlen_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
                             int32_t num_heads, int32_t head_dim, double scale, int32_t causal,
                             const int32_t *rows, int64_t n_rows,
                             double *out, double *lse, int32_t nthreads)
 {
-    if (batch <= 0 || num_heads <= 0 || head_dim <= 0) return -1;
-    for (int64_t r = 0; r < n_rows; r++) {
-        if (rows[2 * r] < cu_q[0] || rows[2 * r] >= cu_q[batch]) return -1;
-        if (rows[2 * r + 1] < 0 || rows[2 * r + 1] >= num_heads) return -1;
-    }
-    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, rows};
-    return run_units(varlen_sample_unit, &c, n_rows, (size_t)max_len(cu_k, batch), nthreads);
+    return oracle_varlen_attn_rows_gqa(q, k, v, cu_q, cu_k, batch, num_heads, num_heads, head_dim, scale, causal,
+                                       rows, n_rows, out, lse, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -35,6 +35,12 @@ def _bind(lib):
     lib.oracle_varlen_attn_rows.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, f64, i32,
                                             i32p, i64, f64p, f64p, i32]
     lib.oracle_varlen_attn_rows.restype = ctypes.c_int
+    lib.oracle_varlen_attn_gqa.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, f64, i32, f64p, f64p,
+                                           i32]
+    lib.oracle_varlen_attn_gqa.restype = ctypes.c_int
+    lib.oracle_varlen_attn_rows_gqa.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, f64, i32,
+                                                i32p, i64, f64p, f64p, i32]
+    lib.oracle_varlen_attn_rows_gqa.restype = ctypes.c_int
     lib.oracle_paged_decode.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32, f64, f64p, i32]
     lib.oracle_paged_decode.restype = ctypes.c_int
     lib.oracle_paged_decode_recurrent.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32,
@@ -72,17 +78,19 @@ def _c(a, dt):
 
 
 def varlen_attn(q, k, v, cu_q, cu_k, scale, causal, nthreads=None, lib=None):
-    """Full oracle: q [Tq,H,D], k/v [Tk,H,D] uint16 bf16 bits; returns
-    (out [Tq,H,D] float64, lse [Tq,H] float64).  Rows of tokens outside every
-    sequence stay NaN."""
+    """Full oracle: q [Tq,H,D], k/v [Tk,Hkv,D] uint16 bf16 bits (Hkv divides
+    H; query head h reads kv head h // (H // Hkv)); returns (out [Tq,H,D]
+    float64, lse [Tq,H] float64).  Rows of tokens outside every sequence stay
+    NaN."""
     lib = lib or load()
     q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
     cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
     Tq, H, D = q.shape
+    Hkv = k.shape[1]
     out = np.full((Tq, H, D), np.nan)
     lse = np.full((Tq, H), np.nan)
-    rc = lib.oracle_varlen_attn(q, k, v, cu_q, cu_k, len(cu_q) - 1, H, D, float(scale), int(bool(causal)),
-                                out, lse, nthreads or default_threads())
+    rc = lib.oracle_varlen_attn_gqa(q, k, v, cu_q, cu_k, len(cu_q) - 1, H, Hkv, D, float(scale),
+                                    int(bool(causal)), out, lse, nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_varlen_attn rejected its arguments")
     return out, lse
@@ -98,9 +106,9 @@ def varlen_attn_rows(q, k, v, cu_q, cu_k, scale, causal, rows, nthreads=None, li
     D = q.shape[2]
     out = np.full((rows.shape[0], D), np.nan)
     lse = np.full((rows.shape[0],), np.nan)
-    rc = lib.oracle_varlen_attn_rows(q, k, v, cu_q, cu_k, len(cu_q) - 1, q.shape[1], D, float(scale),
-                                     int(bool(causal)), rows, rows.shape[0], out, lse,
-                                     nthreads or default_threads())
+    rc = lib.oracle_varlen_attn_rows_gqa(q, k, v, cu_q, cu_k, len(cu_q) - 1, q.shape[1], k.shape[1], D,
+                                         float(scale), int(bool(causal)), rows, rows.shape[0], out, lse,
+                                         nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_varlen_attn_rows rejected its arguments")
     return out, lse

@@ -26,10 +26,13 @@ from variable_length_flashattention_amd.inputs import (bf16_bits, bf16_to_f32, c
 def brute_force_varlen(q, k, v, cu_q, cu_k, scale, causal):
     """softmax over the whole packed [Tq x Tk] score matrix with a block
     diagonal (same-sequence) mask and the bottom-right causal rule, summed with
-    math.fsum.  Written against the definition, not the oracle's loops."""
+    math.fsum.  Written against the definition, not the oracle's loops.  k, v
+    may have fewer heads than q: query head h uses kv head h // (H // Hkv),
+    the contiguous grouping of the decode page."""
     qf, kf, vf = (bf16_to_f32(x).astype(np.float64) for x in (q, k, v))
     Tq, H, D = qf.shape
     Tk = kf.shape[0]
+    R = H // kf.shape[1]
     B = len(cu_q) - 1
     seq_q = np.full(Tq, -1)
     seq_k = np.full(Tk, -1)
@@ -52,7 +55,7 @@ def brute_force_varlen(q, k, v, cu_q, cu_k, scale, causal):
                 j = tk - cu_k[b]
                 if causal and j > i + Lk - Lq:
                     continue
-                logits.append((scale * math.fsum(qf[tq, h, d] * kf[tk, h, d] for d in range(D)), tk))
+                logits.append((scale * math.fsum(qf[tq, h, d] * kf[tk, h // R, d] for d in range(D)), tk))
             if not logits:
                 out[tq, h] = 0.0
                 lse[tq, h] = -math.inf
@@ -61,7 +64,7 @@ def brute_force_varlen(q, k, v, cu_q, cu_k, scale, causal):
             w = [(math.exp(s - M), tk) for s, tk in logits]
             Z = math.fsum(x for x, _ in w)
             for d in range(D):
-                out[tq, h, d] = math.fsum(x * vf[tk, h, d] for x, tk in w) / Z
+                out[tq, h, d] = math.fsum(x * vf[tk, h // R, d] for x, tk in w) / Z
             lse[tq, h] = M + math.log(Z)
     return out, lse
 
@@ -75,13 +78,13 @@ def _close(a, b, tol, what):
     assert np.all(ok), f"{what}: max diff {np.nanmax(np.where(ok, 0, np.abs(a - b)))}"
 
 
-def _random_case(rng, B, H, D, max_len, allow_short_k=True):
+def _random_case(rng, B, H, D, max_len, allow_short_k=True, Hkv=None):
     lq = rng.integers(0, max_len + 1, size=B)
     if allow_short_k:
         lk = rng.integers(0, max_len + 1, size=B)
     else:
         lk = lq + rng.integers(0, 4, size=B)
-    return varlen_case("rand", lq, lk, H, D, int(rng.integers(1 << 30)), False, rng=rng)
+    return varlen_case("rand", lq, lk, H, D, int(rng.integers(1 << 30)), False, rng=rng, num_kv_heads=Hkv)
 
 
 # --- prefill pins -----------------------------------------------------------------
@@ -238,6 +241,26 @@ def _small_decode(seed, ctx, Hq=4, Hkv=2, D=8, BS=4, max_blocks=None):
     return decode_case("d", ctx, Hq, Hkv, D, BS, seed, max_blocks=max_blocks)
 
 
+def pin_gqa_prefill(lib):
+    """Grouped-query prefill (query head h reads kv head h // (H // Hkv), the
+    grouping of step_tile_ref in "spark_storage/attention_ref.rs"): equals the
+    brute force on tiny packs, and equals plain multi-head attention on K/V
+    whose heads are repeated H // Hkv times, bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    for trial, (H, Hkv) in enumerate([(4, 2), (4, 1), (6, 3), (6, 2)]):
+        c = _random_case(rng, B=3, H=H, D=8, max_len=7, Hkv=Hkv)
+        for causal in (False, True):
+            o1, l1 = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+            o2, l2 = brute_force_varlen(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+            _close(o1, o2, 1e-12, f"gqa out trial {trial} causal {causal}")
+            _close(l1, l2, 1e-12, f"gqa lse trial {trial} causal {causal}")
+            R = H // Hkv
+            o3, l3 = O.varlen_attn(c.q, np.repeat(c.k, R, axis=1), np.repeat(c.v, R, axis=1), c.cu_q, c.cu_k,
+                                   c.scale, causal, lib=lib)
+            assert np.array_equal(o1, o3, equal_nan=True) and np.array_equal(l1, l3, equal_nan=True), \
+                f"gqa vs repeated heads, trial {trial}"
+
+
 def pin_decode_direct_equals_recurrence(lib):
     """The direct softmax definition and the decode page's per-token (m, l, o)
     recurrence with state carried across tiles agree to fp64 rounding."""
@@ -358,6 +381,7 @@ ALL_PINS = [
     pin_sequence_isolation_and_order,
     pin_scale_homogeneity,
     pin_sampled_rows_match_full,
+    pin_gqa_prefill,
     pin_decode_direct_equals_recurrence,
     pin_decode_equals_varlen_single_query,
     pin_decode_closed_forms,

@@ -22,10 +22,11 @@ MUTANTS = [
     ("lse_missing_max", "*lse_out = M + log(Z);", "*lse_out = log(Z);"),
     ("no_max_subtraction", "Z += exp(scratch[j] - M);", "Z += exp(scratch[j]);"),
     ("empty_row_lse_zero", "*lse_out = -INFINITY;\n        return;", "*lse_out = 0.0;\n        return;"),
-    ("key_head_ignored", "const uint16_t *krow = c->k + ((k0 + j) * H + h) * D;",
-     "const uint16_t *krow = c->k + ((k0 + j) * H + 0) * D;"),
-    ("value_from_query_offset", "const uint16_t *vrow = c->v + ((k0 + j) * H + h) * D;",
-     "const uint16_t *vrow = c->v + ((q0 + j) * H + h) * D;"),
+    ("key_head_ignored", "const uint16_t *krow = c->k + ((k0 + j) * Hkv + kh) * D;",
+     "const uint16_t *krow = c->k + ((k0 + j) * Hkv + 0) * D;"),
+    ("value_from_query_offset", "const uint16_t *vrow = c->v + ((k0 + j) * Hkv + kh) * D;",
+     "const uint16_t *vrow = c->v + ((q0 + j) * Hkv + kh) * D;"),
+    ("gqa_prefill_interleaved", "const int64_t kh = h / (H / Hkv);", "const int64_t kh = h % Hkv;"),
     ("weights_not_normalised", "const double w = exp(scratch[j] - M) / Z;",
      "const double w = exp(scratch[j] - M);"),
     ("gqa_interleaved", "const int32_t kh = qh / (c->Hq / c->Hkv);\n    const int64_t ctx = c->context_lens[s], D = c->D;\n    const uint16_t *qrow = c->q + ((int64_t)s * c->Hq + qh) * D;\n    double *o = ",

@@ -62,6 +62,10 @@ class VarlenCase:
         return self.q.shape[2]
 
     @property
+    def num_kv_heads(self) -> int:
+        return self.k.shape[1]
+
+    @property
     def max_seqlen_q(self) -> int:
         return int(np.max(np.diff(self.cu_q))) if self.batch else 0
 
@@ -77,12 +81,15 @@ def cu_from_lengths(lengths) -> np.ndarray:
 
 
 def varlen_case(name, lengths_q, lengths_k, num_heads, head_dim, seed, causal, q_mult=1.0,
-                scale=None, rng=None, recipe="") -> VarlenCase:
+                scale=None, rng=None, recipe="", num_kv_heads=None) -> VarlenCase:
+    """k and v carry num_kv_heads heads (default: num_heads); grouped-query
+    cases use num_kv_heads < num_heads."""
     rng = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
     cu_q, cu_k = cu_from_lengths(lengths_q), cu_from_lengths(lengths_k)
+    hkv = num_heads if num_kv_heads is None else num_kv_heads
     q = normal_bf16(rng, (int(cu_q[-1]), num_heads, head_dim), q_mult)
-    k = normal_bf16(rng, (int(cu_k[-1]), num_heads, head_dim))
-    v = normal_bf16(rng, (int(cu_k[-1]), num_heads, head_dim))
+    k = normal_bf16(rng, (int(cu_k[-1]), hkv, head_dim))
+    v = normal_bf16(rng, (int(cu_k[-1]), hkv, head_dim))
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     return VarlenCase(name, q, k, v, cu_q, cu_k, float(scale), bool(causal), seed, recipe)
