@@ -99,8 +99,13 @@ class VarlenRun:
 
     def __call__(self):
         c = self.case
-        self.rra.rra_varlen_attn_fwd(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
-                                     c.max_seqlen_q, c.batch, c.num_heads, c.head_dim, c.scale, c.causal)
+        if c.num_kv_heads == c.num_heads:
+            self.rra.rra_varlen_attn_fwd(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
+                                         c.max_seqlen_q, c.batch, c.num_heads, c.head_dim, c.scale, c.causal)
+        else:
+            self.rra.rra_varlen_attn_fwd_gqa(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
+                                             c.max_seqlen_q, c.batch, c.num_heads, c.num_kv_heads, c.head_dim,
+                                             c.scale, c.causal)
 
 
 class DecodeRun:
@@ -254,6 +259,7 @@ def main():
         for name, case, bound in [
             ("tiny_causal", I.tiny(True), "latency"), ("tiny_noncausal", I.tiny(False), "latency"),
             ("skewed", I.skewed(), "mfma"),
+            ("mixed_gqa_32q_8kv", I.mixed_gqa(), "mfma"),
             ("many_short_d64_causal", I.many_short(64, True), "hbm"),
             ("many_short_d64_noncausal", I.many_short(64, False), "hbm"),
             ("many_short_d256_causal", I.many_short(256, True), "hbm"),

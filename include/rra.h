@@ -73,6 +73,20 @@ int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *o
                             int32_t max_seqlen_q, int32_t batch, int32_t num_heads,
                             int32_t head_dim, float softmax_scale, int32_t causal, void *stream);
 
+/*
+ * Grouped-query variant: k and v are [total_k, num_kv_heads, head_dim] bf16
+ * and query head h reads kv head h / (num_heads / num_kv_heads) (contiguous
+ * groups, the grouping of [DECODE] step_tile_ref; num_kv_heads == 1 is
+ * multi-query attention).  num_kv_heads must be > 0 and divide num_heads
+ * (else RRA_ERR_INVALID_ARG).  Everything else is as rra_varlen_attn_fwd,
+ * which is this call with num_kv_heads == num_heads.
+ */
+int32_t rra_varlen_attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *lse,
+                                const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t batch, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                                int32_t causal, void *stream);
+
 /* Query rows per work item of rra_varlen_attn_fwd for this head_dim and
  * max_seqlen_q (0 if head_dim is unsupported or max_seqlen_q < 0).  Work
  * items are (sequence, query tile, head). */

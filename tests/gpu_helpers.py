@@ -43,9 +43,13 @@ def run_varlen(case, causal=None, poison=True):
         out.view(torch.int16).fill_(0x7FC0)  # bf16 NaN
         lse.fill_(float("nan"))
     say(f"  launch rra_varlen_attn_fwd case={case.name} seed={case.seed} Tq={q.shape[0]} Tk={k.shape[0]} "
-        f"H={q.shape[1]} D={q.shape[2]} B={case.batch} causal={causal}")
-    rra.rra_varlen_attn_fwd(q, k, v, out, lse, cu_q, cu_k, case.max_seqlen_q, case.batch, q.shape[1], q.shape[2],
-                            case.scale, causal)
+        f"H={q.shape[1]} Hkv={k.shape[1]} D={q.shape[2]} B={case.batch} causal={causal}")
+    if k.shape[1] == q.shape[1]:
+        rra.rra_varlen_attn_fwd(q, k, v, out, lse, cu_q, cu_k, case.max_seqlen_q, case.batch, q.shape[1],
+                                q.shape[2], case.scale, causal)
+    else:
+        rra.rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_q, cu_k, case.max_seqlen_q, case.batch, q.shape[1],
+                                    k.shape[1], q.shape[2], case.scale, causal)
     torch.cuda.synchronize()
     return host_f64(out), lse.cpu().numpy().astype(np.float64)
 

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ("rra_varlen_attn_fwd", "rra_paged_decode_attn", "rra_paged_decode_workspace_bytes",
+    for n in ("rra_varlen_attn_fwd", "rra_varlen_attn_fwd_gqa", "rra_paged_decode_attn",
+              "rra_paged_decode_workspace_bytes",
               "rra_status_string", "rra_varlen_block_q"):
         assert n in names
 
@@ -79,6 +80,23 @@ def varlen_status(lib, **kw):
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen_status(lib, **kw) == status
+
+
+def varlen_gqa_status(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cuq=FAKE, cuk=FAKE, maxq=16, batch=2, H=8, Hkv=2, D=128,
+                scale=0.1, causal=1)
+    args.update(kw)
+    return lib.rra_varlen_attn_fwd_gqa(args["q"], args["k"], args["v"], args["out"], args["lse"], args["cuq"],
+                                       args["cuk"], args["maxq"], args["batch"], args["H"], args["Hkv"], args["D"],
+                                       args["scale"], args["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=0), 1), (dict(Hkv=-2), 1), (dict(Hkv=3), 1), (dict(H=8, Hkv=16), 1), (dict(H=0), 1),
+    (dict(D=96), 2), (dict(k=FAKE + 2), 1), (dict(batch=0), 0), (dict(maxq=0, Hkv=3), 1),
+])
+def test_varlen_gqa_validation(lib, kw, status):
+    assert varlen_gqa_status(lib, **kw) == status
 
 
 def decode_status(lib, **kw):

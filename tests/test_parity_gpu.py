@@ -43,6 +43,37 @@ def test_edge_cases(case, causal):
     compare(out, lse, ro, rl, f"{name} causal={causal}")
 
 
+GQA_CASES = [
+    # name, q lengths, k lengths, H, Hkv, D: query head h reads kv head h // (H // Hkv)
+    ("gqa4_d128", [1, 127, 300, 129], [1, 127, 340, 129], 8, 2, 128),
+    ("gqa8_d64", [64, 200, 5, 0, 90], [64, 230, 5, 3, 90], 16, 2, 64),
+    ("mqa_d128", [150, 33], [150, 80], 8, 1, 128),
+    ("gqa3_d256", [1, 70, 160], [1, 70, 170], 6, 2, 256),
+    ("gqa_k_shorter", [40, 200], [5, 64], 4, 2, 128),   # fully masked rows under causal
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=[e[0] for e in GQA_CASES])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_cases(case, causal):
+    name, lq, lk, H, Hkv, D = case
+    c = I.varlen_case(name, lq, lk, H, D, seed=zlib.crc32(name.encode()) % 10000, causal=causal, num_kv_heads=Hkv)
+    out, lse = run_varlen(c)
+    ro, rl = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+    compare(out, lse, ro, rl, f"{name} causal={causal}")
+
+
+def test_gqa_full_size_sampled():
+    """The mixed workload's lengths with 32 query heads over 8 kv heads: every
+    row written, sampled rows against the oracle."""
+    c = I.mixed_gqa()
+    out, lse = run_varlen(c)
+    assert np.all(np.isfinite(lse)), "some (token, head) row was not written"
+    rows = sample_rows(c)
+    ro, rl = O.varlen_attn_rows(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True, rows)
+    compare(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, f"mixed_gqa rows={len(rows)}")
+
+
 def test_scale_and_large_logits():
     """q scaled x8 and a large softmax scale: peaked rows, max subtraction matters."""
     c = I.varlen_case("peaked", [33, 200], [33, 260], 2, 128, seed=77, causal=True, q_mult=8.0, scale=0.5)

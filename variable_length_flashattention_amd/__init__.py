@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     load_library,
     rra_status_string,
     rra_varlen_attn_fwd,
+    rra_varlen_attn_fwd_gqa,
     rra_varlen_block_q,
     rra_paged_decode_attn,
     rra_paged_decode_workspace_bytes,

@@ -49,6 +49,8 @@ def load_library():
     lib.rra_status_string.restype = ctypes.c_char_p
     lib.rra_varlen_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.rra_varlen_attn_fwd.restype = i32
+    lib.rra_varlen_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.rra_varlen_attn_fwd_gqa.restype = i32
     lib.rra_varlen_block_q.argtypes = [i32, i32]
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
@@ -102,6 +104,15 @@ def rra_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     _check("rra_varlen_attn_fwd", st)
 
 
+def rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, batch, num_heads,
+                            num_kv_heads, head_dim, softmax_scale, causal, stream=None):
+    st = load_library().rra_varlen_attn_fwd_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        int(max_seqlen_q), int(batch), int(num_heads), int(num_kv_heads), int(head_dim), float(softmax_scale),
+        int(bool(causal)), _stream(stream))
+    _check("rra_varlen_attn_fwd_gqa", st)
+
+
 def rra_paged_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
     return int(load_library().rra_paged_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(num_kv_heads),
                                                                int(head_dim)))
@@ -139,8 +150,9 @@ def rra_debug_paged_gather(pool, block_table, context_lens, dense, num_seqs, num
 
 def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_scale, causal, out=None,
                     lse=None, stream=None):
-    """q [Tq,H,D], k/v [Tk,H,D] bf16 CUDA tensors; cu_seqlens int32 CUDA
-    tensors.  Returns (out bf16 [Tq,H,D], lse fp32 [Tq,H])."""
+    """q [Tq,H,D], k/v [Tk,Hkv,D] bf16 CUDA tensors (Hkv divides H; Hkv < H
+    is grouped-query attention); cu_seqlens int32 CUDA tensors.  Returns
+    (out bf16 [Tq,H,D], lse fp32 [Tq,H])."""
     import torch
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
         raise TypeError("q, k, v must be bfloat16")
@@ -149,8 +161,9 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_s
     for t in (q, k, v, cu_seqlens_q, cu_seqlens_k):
         if not t.is_contiguous() or not t.is_cuda:
             raise ValueError("all tensors must be contiguous device tensors")
-    if q.dim() != 3 or k.shape != v.shape or k.dim() != 3 or q.shape[1:] != k.shape[1:]:
-        raise ValueError("q must be [Tq,H,D] and k, v [Tk,H,D]")
+    if q.dim() != 3 or k.shape != v.shape or k.dim() != 3 or q.shape[2] != k.shape[2] or k.shape[1] == 0 \
+            or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("q must be [Tq,H,D] and k, v [Tk,Hkv,D] with Hkv dividing H")
     if cu_seqlens_q.numel() != cu_seqlens_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     Tq, H, D = q.shape
@@ -158,8 +171,8 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_s
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
-    rra_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, cu_seqlens_q.numel() - 1,
-                        H, D, softmax_scale, causal, stream)
+    rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, cu_seqlens_q.numel() - 1,
+                            H, k.shape[1], D, softmax_scale, causal, stream)
     return out, lse
 
 

@@ -54,12 +54,13 @@ int32_t rra_varlen_block_q(int32_t head_dim, int32_t max_seqlen_q)
     return supported_head_dim(head_dim) && max_seqlen_q >= 0 ? varlen_block_q(head_dim, max_seqlen_q) : 0;
 }
 
-int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
-                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
-                            int32_t batch, int32_t num_heads, int32_t head_dim, float softmax_scale,
-                            int32_t causal, void *stream)
+int32_t rra_varlen_attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *lse,
+                                const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
+                                int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                float softmax_scale, int32_t causal, void *stream)
 {
     if (batch < 0 || num_heads <= 0 || head_dim <= 0 || max_seqlen_q < 0) return RRA_ERR_INVALID_ARG;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return RRA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return RRA_ERR_INVALID_ARG;
     if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
     if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
@@ -78,6 +79,8 @@ int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *o
     a.cu_k = cu_seqlens_k;
     a.batch = batch;
     a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.gqa_ratio = num_heads / num_kv_heads;
     a.block_q = varlen_block_q(head_dim, max_seqlen_q);
     const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + a.block_q - 1) / a.block_q;
     a.levels = (int32_t)tiles_per_seq;
@@ -85,6 +88,15 @@ int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *o
     a.scale = softmax_scale;
     a.scale_log2 = softmax_scale * kLog2e;
     return hip_status(launch_varlen_fwd(a, head_dim, causal == 1, device_cus(), static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t batch, int32_t num_heads, int32_t head_dim, float softmax_scale,
+                            int32_t causal, void *stream)
+{
+    return rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, batch, num_heads,
+                                   num_heads, head_dim, softmax_scale, causal, stream);
 }
 
 int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,

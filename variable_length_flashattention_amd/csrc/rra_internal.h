@@ -26,6 +26,8 @@ struct VarlenArgs {
     float *lse;
     const int32_t *cu_q, *cu_k;
     int32_t batch, num_heads;
+    int32_t num_kv_heads;  // k and v heads; query head h reads kv head h / gqa_ratio
+    int32_t gqa_ratio;     // num_heads / num_kv_heads
     int32_t block_q;     // query rows per work item (varlen_block_q)
     int32_t levels;      // ceil(max_seqlen_q / block_q): upper bound on tiles per sequence
     int64_t n_items;     // batch * levels * num_heads: upper bound on real items

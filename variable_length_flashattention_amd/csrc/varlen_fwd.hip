@@ -2,8 +2,12 @@
 //
 // Method: "Varlen Flash Attention Implementation Plan", Task 1 (the online
 // softmax over key tiles: running row max m and denominator l in fp32,
-// rescaling of the accumulator, out = acc / l, lse = m + ln l).  The work
-// decomposition, tile shapes and data movement here are this library's own.
+// rescaling of the accumulator, out = acc / l, lse = m + ln l).  Grouped-query
+// attention reads kv head h / (H / Hkv) for query head h, the grouping of
+// step_tile_ref in "spark_storage/attention_ref.rs"; heads are innermost in
+// the work list, so the query heads of one kv head run side by side and share
+// its K/V in L2.  The work decomposition, tile shapes and data movement here
+// are this library's own.
 //
 // One workgroup of NW waves owns a work item (sequence b, query tile qt,
 // head h) of BQ = 32*NW query rows; each wave owns a 32-row block of the tile.
@@ -128,14 +132,15 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         constexpr int NKO = RPL % 16 == 0 ? 1 : 16 / RPL;  // distinct K swizzles over the loads
         static_assert(RPL % 4 == 0 && (RPL % 16 == 0 || 16 % RPL == 0), "swizzle period");
         const int srow0 = (wave * 1024 + lane * 16) / ROWB, pch = (lane * 16 % ROWB) / 16;
-        const int row_bytes = H * D * 2;              // bytes from one token to the next
+        const int row_bytes = a.num_kv_heads * D * 2;  // bytes from one K/V token to the next
         uint32_t lane_k[NKO];
 #pragma unroll
         for (int j = 0; j < NKO; j++)
             lane_k[j] = (uint32_t)(srow0 * row_bytes + 16 * (pch ^ T::swz_k(srow0 + j * RPL)));
         const uint32_t lane_v = (uint32_t)(srow0 * row_bytes + 16 * (pch ^ T::swz_v(srow0)));
-        const uint8_t *kseq = reinterpret_cast<const uint8_t *>(a.k + ((int64_t)k0 * H + h) * D);
-        const uint8_t *vseq = reinterpret_cast<const uint8_t *>(a.v + ((int64_t)k0 * H + h) * D);
+        const int kh = h / a.gqa_ratio;  // the kv head of query head h
+        const uint8_t *kseq = reinterpret_cast<const uint8_t *>(a.k + ((int64_t)k0 * a.num_kv_heads + kh) * D);
+        const uint8_t *vseq = reinterpret_cast<const uint8_t *>(a.v + ((int64_t)k0 * a.num_kv_heads + kh) * D);
         auto stage = [&](int kt, uint8_t *kb, uint8_t *vb) {
             const int64_t toff = (int64_t)kt * BK * row_bytes;
             const __amdgpu_buffer_rsrc_t kr = raw_buffer(kseq + toff), vr = raw_buffer(vseq + toff);

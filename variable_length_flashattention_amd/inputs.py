@@ -111,6 +111,15 @@ def mixed(seed: int = 2001, causal: bool = True) -> VarlenCase:
                        recipe="16 lengths U[1,2048] (q=k); H=32; D=128; N(0,1) bf16; causal")
 
 
+def mixed_gqa(seed: int = 2001, causal: bool = True) -> VarlenCase:
+    """The mixed workload's lengths (seed 2001) with grouped-query K/V: 32 query
+    heads over 8 kv heads, head_dim 128."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = rng.integers(1, 2049, size=16)
+    return varlen_case("mixed_gqa", lengths, lengths, 32, 128, seed, causal, rng=rng, num_kv_heads=8,
+                       recipe="16 lengths U[1,2048] (q=k); H=32, Hkv=8; D=128; N(0,1) bf16; causal")
+
+
 def skewed(seed: int = 3001, causal: bool = True) -> VarlenCase:
     """q lengths {8192,1024,128,7}, k lengths {8192,3072,128,519}, 16 heads, head_dim 128."""
     return varlen_case("skewed", [8192, 1024, 128, 7], [8192, 3072, 128, 519], 16, 128, seed, causal,
@@ -214,9 +223,9 @@ def varlen_flops(case: VarlenCase) -> int:
 
 def varlen_bytes(case: VarlenCase) -> int:
     """Compulsory HBM bytes: read q, k, v once; write out and lse; read cu_seqlens."""
-    H, D = case.num_heads, case.head_dim
+    H, Hkv, D = case.num_heads, case.num_kv_heads, case.head_dim
     Tq, Tk = int(case.cu_q[-1]), int(case.cu_k[-1])
-    return 2 * H * D * (2 * Tq + 2 * Tk) + 4 * Tq * H + 8 * (case.batch + 1)
+    return 2 * D * (2 * H * Tq + 2 * Hkv * Tk) + 4 * Tq * H + 8 * (case.batch + 1)
 
 
 def decode_bytes(case: DecodeCase) -> int:
