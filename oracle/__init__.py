@@ -11,6 +11,9 @@ from .oracle import (  # noqa: F401
     varlen_attn_rows,
     paged_decode,
     paged_decode_recurrent,
+    decode_state_init,
+    paged_decode_step,
+    paged_decode_finalize,
     paged_gather,
     varlen_tile_map,
     default_threads,

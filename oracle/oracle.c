@@ -312,6 +312,18 @@ static void decode_direct_unit(void *p, int64_t unit, double *scratch)
     }
 }
 
+/* One token of the decode page's recurrence (step_tile_ref): score x, value
+ * row vr; the state (m, l, o) moves to the new running max. */
+static void fold_token(double *m, double *l, double *o, double x, const uint16_t *vr, int64_t D)
+{
+    const double m_new = x > *m ? x : *m;
+    const double scale_old = exp(*m - m_new);
+    const double scale_new = exp(x - m_new);
+    *l = *l * scale_old + scale_new;
+    for (int64_t d = 0; d < D; d++) o[d] = o[d] * scale_old + scale_new * bf16_value(vr[d]);
+    *m = m_new;
+}
+
 /* The decode page's route: running state (m, l, o) starting at (-inf, 0, 0),
  * one token at a time in block-table order:
  *   m' = max(m, x);  l = l*exp(m - m') + exp(x - m');  o = o*exp(m - m') + exp(x - m')*v;  m = m'
@@ -346,13 +358,7 @@ static void decode_recurrent_unit(void *p, int64_t unit, double *scratch)
                 const uint16_t *vr = pool_row(c, c->v_pool, s, t, kh);
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(kr[d]);
-                const double x = c->scale * dot;
-                const double m_new = x > m ? x : m;
-                const double scale_old = exp(m - m_new);
-                const double scale_new = exp(x - m_new);
-                l = l * scale_old + scale_new;
-                for (int64_t d = 0; d < D; d++) o[d] = o[d] * scale_old + scale_new * bf16_value(vr[d]);
-                m = m_new;
+                fold_token(&m, &l, o, c->scale * dot, vr, D);
             }
         }
         st_m = m; st_l = l; /* store state */
@@ -404,6 +410,77 @@ int oracle_paged_decode_recurrent(const uint16_t *q, const uint16_t *k_pool, con
     decode_ctx c = {q, k_pool, v_pool, block_table, context_lens, num_seqs, num_q_heads, num_kv_heads,
                     head_dim, block_size, max_blocks_per_seq, scale, tile_capacity, out};
     return run_units(decode_recurrent_unit, &c, (int64_t)num_seqs * num_q_heads, (size_t)head_dim, nthreads);
+}
+
+/* The decode page's stateful interface.  The caller owns the state
+ * (AttnState): m, l [S, Hq] and o [S, Hq, D], starting at (-inf, 0, 0).  A
+ * step (step_tile_ref) folds, for every sequence s, the tokens of the blocks
+ * tile_blocks[s, 0 .. tile_block_counts[s]) in order, every token of each
+ * block unless token_counts is given, in which case the tile ends after
+ * token_counts[s] tokens (a partly filled last block).  finalize_ref turns
+ * the state into out = o / l (0 where l == 0). */
+typedef struct {
+    double *m, *l, *o;
+    const uint16_t *q, *k_pool, *v_pool;
+    const int32_t *tile_blocks, *tile_block_counts, *token_counts;
+    int32_t S, Hq, Hkv, D, BS, tile_capacity;
+    double scale;
+} step_ctx;
+
+static void decode_step_unit(void *p, int64_t unit, double *scratch)
+{
+    (void)scratch;
+    const step_ctx *c = (const step_ctx *)p;
+    const int32_t s = (int32_t)(unit / c->Hq), qh = (int32_t)(unit % c->Hq);
+    const int32_t kh = qh / (c->Hq / c->Hkv);
+    const int64_t D = c->D;
+    const uint16_t *qrow = c->q + ((int64_t)s * c->Hq + qh) * D;
+    double m = c->m[unit], l = c->l[unit];
+    double *o = c->o + unit * D;
+    const int64_t n_tok = c->token_counts ? c->token_counts[s] : (int64_t)c->tile_block_counts[s] * c->BS;
+    for (int64_t b = 0; b < c->tile_block_counts[s]; b++) {
+        const int64_t blk = c->tile_blocks[(int64_t)s * c->tile_capacity + b];
+        for (int64_t slot = 0; slot < c->BS; slot++) {
+            if (b * c->BS + slot >= n_tok) break;
+            const uint16_t *kr = c->k_pool + ((blk * c->BS + slot) * c->Hkv + kh) * D;
+            const uint16_t *vr = c->v_pool + ((blk * c->BS + slot) * c->Hkv + kh) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(kr[d]);
+            fold_token(&m, &l, o, c->scale * dot, vr, D);
+        }
+    }
+    c->m[unit] = m;
+    c->l[unit] = l;
+}
+
+int oracle_paged_decode_step(double *state_m, double *state_l, double *state_o,
+                             const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                             const int32_t *tile_blocks, const int32_t *tile_block_counts,
+                             const int32_t *token_counts, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t tile_capacity,
+                             double scale, int32_t nthreads)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0) return -1;
+    if (num_q_heads % num_kv_heads != 0 || tile_capacity < 0) return -1;
+    for (int32_t s = 0; s < num_seqs; s++) {
+        if (tile_block_counts[s] < 0 || tile_block_counts[s] > tile_capacity) return -1;
+        if (token_counts && (token_counts[s] < 0 || token_counts[s] > (int64_t)tile_block_counts[s] * block_size))
+            return -1;
+    }
+    step_ctx c = {state_m, state_l, state_o, q, k_pool, v_pool, tile_blocks, tile_block_counts, token_counts,
+                  num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, tile_capacity, scale};
+    return run_units(decode_step_unit, &c, (int64_t)num_seqs * num_q_heads, 1, nthreads);
+}
+
+int oracle_paged_decode_finalize(const double *state_l, const double *state_o, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t head_dim, double *out)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return -1;
+    for (int64_t u = 0; u < (int64_t)num_seqs * num_q_heads; u++) {
+        const double inv_l = state_l[u] > 0.0 ? 1.0 / state_l[u] : 0.0;
+        for (int64_t d = 0; d < head_dim; d++) out[u * head_dim + d] = state_o[u * head_dim + d] * inv_l;
+    }
+    return 0;
 }
 
 /* Gather of the visible pool rows of every sequence into a dense buffer

@@ -46,6 +46,11 @@ def _bind(lib):
     lib.oracle_paged_decode_recurrent.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32,
                                                   f64, i32, f64p, i32]
     lib.oracle_paged_decode_recurrent.restype = ctypes.c_int
+    lib.oracle_paged_decode_step.argtypes = [f64p, f64p, f64p, u16p, u16p, u16p, i32p, i32p, ctypes.c_void_p,
+                                             i32, i32, i32, i32, i32, i32, f64, i32]
+    lib.oracle_paged_decode_step.restype = ctypes.c_int
+    lib.oracle_paged_decode_finalize.argtypes = [f64p, f64p, i32, i32, i32, f64p]
+    lib.oracle_paged_decode_finalize.restype = ctypes.c_int
     lib.oracle_paged_gather.argtypes = [u16p, i32p, i32p, i32, i32, i32, i32, i32, u16p]
     lib.oracle_paged_gather.restype = ctypes.c_int
     lib.oracle_varlen_tile_map.argtypes = [i32p, i32, i32, i32, i32p, i64]
@@ -147,6 +152,43 @@ def paged_decode_recurrent(q, k_pool, v_pool, block_table, context_lens, scale, 
                                            int(tile_capacity), out, nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_paged_decode_recurrent rejected its arguments")
+    return out
+
+
+def decode_state_init(num_seqs, num_q_heads, head_dim):
+    """The decode page's initial AttnState: m = -inf, l = 0, o = 0 (fp64 here)."""
+    return (np.full((num_seqs, num_q_heads), -np.inf), np.zeros((num_seqs, num_q_heads)),
+            np.zeros((num_seqs, num_q_heads, head_dim)))
+
+
+def paged_decode_step(state, q, k_pool, v_pool, tile_blocks, tile_block_counts, scale, token_counts=None,
+                      nthreads=None, lib=None):
+    """One step_tile_ref: fold the listed blocks (tile_blocks [S, cap] int32,
+    tile_block_counts [S]; token_counts [S] cuts the tile) into the state
+    (m, l, o), in place."""
+    lib = lib or load()
+    m, l, o = state
+    q, k_pool, v_pool = _c(q, np.uint16), _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    tb, tc = _c(tile_blocks, np.int32), _c(tile_block_counts, np.int32)
+    S, Hq, D = q.shape
+    _, BS, Hkv, _ = k_pool.shape
+    tok = None if token_counts is None else _c(token_counts, np.int32)
+    rc = lib.oracle_paged_decode_step(m, l, o, q, k_pool, v_pool, tb, tc,
+                                      None if tok is None else tok.ctypes.data_as(ctypes.c_void_p),
+                                      S, Hq, Hkv, D, BS, tb.shape[1], float(scale), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_paged_decode_step rejected its arguments")
+    return state
+
+
+def paged_decode_finalize(state, lib=None):
+    """finalize_ref: out = o / l, 0 where l == 0."""
+    lib = lib or load()
+    m, l, o = state
+    S, Hq, D = o.shape
+    out = np.full((S, Hq, D), np.nan)
+    if lib.oracle_paged_decode_finalize(l, o, S, Hq, D, out) != 0:
+        raise ValueError("oracle_paged_decode_finalize rejected its arguments")
     return out
 
 

@@ -291,6 +291,66 @@ def pin_decode_equals_varlen_single_query(lib):
     _close(out, o2, 1e-12, "decode vs varlen")
 
 
+def split_into_tiles(case, rng, max_cap):
+    """Cut every sequence's block list into consecutive tiles of random sizes
+    (1..max_cap blocks, possibly empty for a sequence); returns a list of
+    (tile_blocks [S, max_cap], tile_block_counts [S], token_counts [S])."""
+    S, BS = case.num_seqs, case.block_size
+    nblk = [(int(c) + BS - 1) // BS for c in case.context_lens]
+    pos = [0] * S
+    tiles = []
+    while any(pos[s] < nblk[s] for s in range(S)):
+        tb = np.full((S, max_cap), -1, dtype=np.int32)
+        cnt = np.zeros(S, dtype=np.int32)
+        tok = np.zeros(S, dtype=np.int32)
+        for s in range(S):
+            take = min(int(rng.integers(0, max_cap + 1)), nblk[s] - pos[s])
+            tb[s, :take] = case.block_table[s, pos[s]:pos[s] + take]
+            cnt[s] = take
+            t0, t1 = pos[s] * BS, min((pos[s] + take) * BS, int(case.context_lens[s]))
+            tok[s] = max(0, t1 - t0)
+            pos[s] += take
+        tiles.append((tb, cnt, tok))
+    return tiles
+
+
+def pin_decode_step(lib):
+    """The stateful interface (AttnState, step_tile_ref, finalize_ref): folding
+    any cut of the context into tiles, step after step from (-inf, 0, 0), then
+    finalizing equals the direct softmax definition; m + ln l is the
+    log-sum-exp of the scaled scores; a state that saw no token finalizes to 0."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    c = _small_decode(31, [0, 1, 5, 16, 17, 40], Hq=4, Hkv=2, D=8, BS=4)
+    ref = O.paged_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale, lib=lib)
+    for trial in range(3):
+        st = O.decode_state_init(c.num_seqs, c.num_q_heads, c.head_dim)
+        for tb, cnt, tok in split_into_tiles(c, rng, max_cap=3):
+            O.paged_decode_step(st, c.q, c.k_pool, c.v_pool, tb, cnt, c.scale, token_counts=tok, lib=lib)
+        out = O.paged_decode_finalize(st, lib=lib)
+        _close(out, ref, 1e-12, f"step trial {trial}")
+        # log-sum-exp of the scaled scores, from the gathered rows
+        qf = bf16_to_f32(c.q).astype(np.float64)
+        R = c.num_q_heads // c.num_kv_heads
+        for s in range(c.num_seqs):
+            ctx = int(c.context_lens[s])
+            t = np.arange(ctx)
+            kk = bf16_to_f32(c.k_pool[c.block_table[s, t // c.block_size], t % c.block_size]).astype(np.float64)
+            for qh in range(c.num_q_heads):
+                if ctx == 0:
+                    assert st[0][s, qh] == -np.inf and st[1][s, qh] == 0.0 and np.all(out[s, qh] == 0.0)
+                    continue
+                x = c.scale * (kk[:, qh // R, :] @ qf[s, qh])
+                lse = x.max() + math.log(math.fsum(np.exp(x - x.max())))
+                _close(st[0][s, qh] + math.log(st[1][s, qh]), lse, 1e-12, f"step lse s={s} qh={qh}")
+    # without token counts every token of the listed blocks counts
+    st = O.decode_state_init(c.num_seqs, c.num_q_heads, c.head_dim)
+    full = c.context_lens - c.context_lens % c.block_size  # whole blocks only
+    nb = full // c.block_size
+    O.paged_decode_step(st, c.q, c.k_pool, c.v_pool, c.block_table, nb, c.scale, lib=lib)
+    ref_full = O.paged_decode(c.q, c.k_pool, c.v_pool, c.block_table, full.astype(np.int32), c.scale, lib=lib)
+    _close(O.paged_decode_finalize(st, lib=lib), ref_full, 1e-12, "step over whole blocks")
+
+
 def pin_decode_closed_forms(lib):
     """ctx 0 -> 0; ctx 1 -> v_0; V constant per kv head kh -> every q head of
     the group qh // (Hq/Hkv) == kh gets that constant."""
@@ -384,6 +444,7 @@ ALL_PINS = [
     pin_gqa_prefill,
     pin_decode_direct_equals_recurrence,
     pin_decode_equals_varlen_single_query,
+    pin_decode_step,
     pin_decode_closed_forms,
     pin_decode_ignores_tail,
     pin_decode_gather,

@@ -34,7 +34,11 @@ MUTANTS = [
     ("decode_reads_whole_last_block", "for (int64_t t = 0; t < ctx; t++) {\n        const uint16_t *kr",
      "for (int64_t t = 0; t < (ctx + c->BS - 1) / c->BS * c->BS; t++) {\n        const uint16_t *kr"),
     ("decode_slot_from_block", "const int64_t slot = t % c->BS;", "const int64_t slot = t / c->BS % c->BS;"),
-    ("recurrence_rescale_sign", "const double scale_old = exp(m - m_new);", "const double scale_old = exp(m_new - m);"),
+    ("recurrence_rescale_sign", "const double scale_old = exp(*m - m_new);", "const double scale_old = exp(m_new - *m);"),
+    ("step_ignores_token_count", "if (b * c->BS + slot >= n_tok) break;", "if (b * c->BS + slot >= c->BS * c->tile_block_counts[s]) break;"),
+    ("step_finalize_unguarded", "const double inv_l = state_l[u] > 0.0 ? 1.0 / state_l[u] : 0.0;",
+     "const double inv_l = 1.0 / state_l[u];"),
+    ("step_state_not_carried", "double m = c->m[unit], l = c->l[unit];", "double m = -INFINITY, l = 0.0;"),
     ("finalize_unguarded", "const double inv_l = st_l > 0.0 ? 1.0 / st_l : 0.0;", "const double inv_l = 1.0 / st_l;"),
     ("tile_levels_ascending", "for (int64_t r = max_tiles - 1; r >= 0; r--) {", "for (int64_t r = 0; r < max_tiles; r++) {"),
     ("tile_count_floor", "const int64_t n = (L + block_q - 1) / block_q;\n            if (n <= r) continue;",
