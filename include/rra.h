@@ -135,6 +135,55 @@ size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
                                         int32_t head_dim);
 
 /*
+ * Stateful decode ([DECODE] AttnState, step_tile_ref, finalize_ref): the
+ * running softmax state of every (sequence, q head) lives in caller-owned
+ * fp32 device buffers, and each step folds one tile of paged K/V into it, so
+ * that a context can arrive in pieces (e.g. as its blocks are produced).
+ *
+ *   state_m       fp32 [num_seqs, num_q_heads]: running max of the scaled
+ *                 scores softmax_scale * q . K_t (-inf before any token)
+ *   state_l       fp32 [num_seqs, num_q_heads]: sum of exp(score - m)
+ *   state_o       fp32 [num_seqs, num_q_heads, head_dim]: sum of
+ *                 exp(score - m) V_t; 16-byte aligned
+ *
+ * rra_paged_decode_state_init sets m = -inf, l = 0, o = 0 (one kernel).
+ *
+ * rra_paged_decode_step folds, for every sequence s, the tokens of this step's
+ * tile into the state, in place:
+ *   tile_blocks        int32 [num_seqs, tile_capacity] device array: the pool
+ *                      blocks of the tile, in token order
+ *   tile_block_counts  int32 [num_seqs] device array: blocks used in the tile
+ *                      (clamped into [0, tile_capacity]; 0 leaves s unchanged)
+ *   tile_token_counts  int32 [num_seqs] device array or NULL: the tile holds
+ *                      the first tile_token_counts[s] tokens of its blocks
+ *                      (clamped into [0, blocks * block_size]); NULL means
+ *                      every slot of every listed block
+ * q, k_pool, v_pool, num_q_heads, num_kv_heads, head_dim, block_size,
+ * softmax_scale and the workspace are as for rra_paged_decode_attn (the
+ * workspace size is rra_paged_decode_workspace_bytes of the same sizes).  The
+ * new tokens' partial states are merged into (m, l, o) with the usual
+ * max-shift.  Steps on one state must be ordered (same stream or
+ * synchronised); any split of a context into tiles gives the same result up
+ * to fp32 rounding.
+ *
+ * rra_paged_decode_finalize writes out (bf16 [num_seqs, num_q_heads,
+ * head_dim], 16-byte aligned) = o / l, and 0 where l == 0 (no token seen).
+ */
+int32_t rra_paged_decode_state_init(float *state_m, float *state_l, float *state_o, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t head_dim, void *stream);
+
+int32_t rra_paged_decode_step(float *state_m, float *state_l, float *state_o, const void *q,
+                              const void *k_pool, const void *v_pool, const int32_t *tile_blocks,
+                              const int32_t *tile_block_counts, const int32_t *tile_token_counts,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t tile_capacity,
+                              float softmax_scale, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+int32_t rra_paged_decode_finalize(const float *state_l, const float *state_o, void *out, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t head_dim, void *stream);
+
+/*
  * Test hooks (integer work, checked bit-exactly against an independent
  * definition).
  *

@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("rra_varlen_attn_fwd", "rra_varlen_attn_fwd_gqa", "rra_paged_decode_attn",
-              "rra_paged_decode_workspace_bytes",
+              "rra_paged_decode_workspace_bytes", "rra_paged_decode_state_init", "rra_paged_decode_step",
+              "rra_paged_decode_finalize",
               "rra_status_string", "rra_varlen_block_q"):
         assert n in names
 
@@ -117,6 +118,44 @@ def decode_status(lib, **kw):
 ])
 def test_decode_validation(lib, kw, status):
     assert decode_status(lib, **kw) == status
+
+
+def step_status(lib, **kw):
+    a = dict(m=FAKE, l=FAKE, o=FAKE, q=FAKE, kp=FAKE, vp=FAKE, tb=FAKE, tc=FAKE, tok=None, S=4, Hq=32, Hkv=8, D=128,
+             BS=16, cap=8, scale=0.1, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.rra_paged_decode_step(a["m"], a["l"], a["o"], a["q"], a["kp"], a["vp"], a["tb"], a["tc"], a["tok"],
+                                     a["S"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["cap"], a["scale"], a["ws"],
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=-1), 1), (dict(Hq=0), 1), (dict(Hq=12, Hkv=8), 1), (dict(BS=0), 1), (dict(cap=-1), 1),
+    (dict(scale=-0.5), 1), (dict(scale=float("inf")), 1),
+    (dict(D=96), 2), (dict(BS=24), 2),
+    (dict(m=None), 1), (dict(l=None), 1), (dict(o=None), 1), (dict(o=FAKE + 4), 1), (dict(tb=None), 1),
+    (dict(tc=None), 1), (dict(q=None), 1), (dict(kp=FAKE + 2), 1),
+    (dict(ws=None), 3), (dict(wsb=64), 3),
+    (dict(S=0), 0), (dict(S=0, m=None, l=None, o=None, ws=None), 0),
+])
+def test_decode_step_validation(lib, kw, status):
+    assert step_status(lib, **kw) == status
+
+
+@pytest.mark.parametrize("fn,args,status", [
+    ("rra_paged_decode_finalize", (FAKE, FAKE, FAKE, -1, 8, 128), 1),
+    ("rra_paged_decode_finalize", (FAKE, FAKE, FAKE, 4, 0, 128), 1),
+    ("rra_paged_decode_finalize", (FAKE, FAKE, FAKE, 4, 8, 80), 2),
+    ("rra_paged_decode_finalize", (None, FAKE, FAKE, 4, 8, 128), 1),
+    ("rra_paged_decode_finalize", (FAKE, FAKE, FAKE + 2, 4, 8, 128), 1),
+    ("rra_paged_decode_finalize", (None, None, None, 0, 8, 128), 0),
+    ("rra_paged_decode_state_init", (FAKE, FAKE, FAKE, -1, 8, 128), 1),
+    ("rra_paged_decode_state_init", (FAKE, FAKE, FAKE, 4, 8, 48), 2),
+    ("rra_paged_decode_state_init", (FAKE, None, FAKE, 4, 8, 128), 1),
+    ("rra_paged_decode_state_init", (None, None, None, 0, 8, 128), 0),
+])
+def test_decode_state_calls_validation(lib, fn, args, status):
+    assert getattr(lib, fn)(*args, None) == status
 
 
 def test_workspace_size(lib):

@@ -14,8 +14,14 @@ from .binding import (  # noqa: F401
     rra_varlen_block_q,
     rra_paged_decode_attn,
     rra_paged_decode_workspace_bytes,
+    rra_paged_decode_state_init,
+    rra_paged_decode_step,
+    rra_paged_decode_finalize,
     rra_debug_varlen_tile_map,
     rra_debug_paged_gather,
     varlen_attn_fwd,
     paged_decode_attn,
+    decode_state_init,
+    paged_decode_step,
+    paged_decode_finalize,
 )

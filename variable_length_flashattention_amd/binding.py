@@ -55,6 +55,13 @@ def load_library():
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.rra_paged_decode_attn.restype = i32
+    lib.rra_paged_decode_state_init.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.rra_paged_decode_state_init.restype = i32
+    lib.rra_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp,
+                                          sz, vp]
+    lib.rra_paged_decode_step.restype = i32
+    lib.rra_paged_decode_finalize.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.rra_paged_decode_finalize.restype = i32
     lib.rra_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.rra_paged_decode_workspace_bytes.restype = sz
     lib.rra_debug_varlen_tile_map.argtypes = [vp, i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64), vp]
@@ -128,6 +135,29 @@ def rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, num
     _check("rra_paged_decode_attn", st)
 
 
+def rra_paged_decode_state_init(state_m, state_l, state_o, num_seqs, num_q_heads, head_dim, stream=None):
+    st = load_library().rra_paged_decode_state_init(_ptr(state_m), _ptr(state_l), _ptr(state_o), int(num_seqs),
+                                                    int(num_q_heads), int(head_dim), _stream(stream))
+    _check("rra_paged_decode_state_init", st)
+
+
+def rra_paged_decode_step(state_m, state_l, state_o, q, k_pool, v_pool, tile_blocks, tile_block_counts,
+                          tile_token_counts, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, tile_capacity,
+                          softmax_scale, workspace, workspace_bytes, stream=None):
+    st = load_library().rra_paged_decode_step(
+        _ptr(state_m), _ptr(state_l), _ptr(state_o), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(tile_blocks),
+        _ptr(tile_block_counts), _ptr(tile_token_counts), int(num_seqs), int(num_q_heads), int(num_kv_heads),
+        int(head_dim), int(block_size), int(tile_capacity), float(softmax_scale), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+    _check("rra_paged_decode_step", st)
+
+
+def rra_paged_decode_finalize(state_l, state_o, out, num_seqs, num_q_heads, head_dim, stream=None):
+    st = load_library().rra_paged_decode_finalize(_ptr(state_l), _ptr(state_o), _ptr(out), int(num_seqs),
+                                                  int(num_q_heads), int(head_dim), _stream(stream))
+    _check("rra_paged_decode_finalize", st)
+
+
 def rra_debug_varlen_tile_map(cu_seqlens_q, batch, num_heads, max_seqlen_q, head_dim, items_out, capacity,
                               stream=None) -> int:
     count = ctypes.c_int64(0)
@@ -181,6 +211,7 @@ def paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, softmax_scal
     """q [S,Hq,D] bf16; pools [NB,BS,Hkv,D] bf16; block_table [S,maxb] int32;
     context_lens [S] int32 (all device tensors).  Returns out bf16 [S,Hq,D]."""
     import torch
+    _decode_checks(q, k_pool, v_pool, (block_table, context_lens))
     S, Hq, D = q.shape
     _, BS, Hkv, _ = k_pool.shape
     MB = block_table.shape[1]
@@ -191,4 +222,61 @@ def paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, softmax_scal
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, S, Hq, Hkv, D, BS, MB, softmax_scale,
                           workspace, workspace.numel() * workspace.element_size(), stream)
+    return out
+
+
+def _decode_checks(q, k_pool, v_pool, index_tensors):
+    import torch
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise TypeError("q, k_pool, v_pool must be bfloat16")
+    for t in index_tensors:
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError("block tables and counts must be int32")
+    for t in (q, k_pool, v_pool) + tuple(index_tensors):
+        if t is not None and (not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("all tensors must be contiguous device tensors")
+    if q.dim() != 3 or k_pool.dim() != 4 or k_pool.shape != v_pool.shape or q.shape[2] != k_pool.shape[3]:
+        raise ValueError("q must be [S,Hq,D] and the pools [NB,BS,Hkv,D]")
+
+
+def decode_state_init(num_seqs, num_q_heads, head_dim, device, stream=None):
+    """A fresh decode state (m, l, o): fp32 device tensors [S,Hq], [S,Hq],
+    [S,Hq,D] holding m = -inf, l = 0, o = 0."""
+    import torch
+    m = torch.empty((num_seqs, num_q_heads), dtype=torch.float32, device=device)
+    l = torch.empty_like(m)
+    o = torch.empty((num_seqs, num_q_heads, head_dim), dtype=torch.float32, device=device)
+    rra_paged_decode_state_init(m, l, o, num_seqs, num_q_heads, head_dim, stream)
+    return m, l, o
+
+
+def paged_decode_step(state, q, k_pool, v_pool, tile_blocks, tile_block_counts, softmax_scale, token_counts=None,
+                      workspace=None, stream=None):
+    """Fold one tile of paged K/V into state = (m, l, o), in place.
+    tile_blocks [S, cap] int32, tile_block_counts [S] int32, token_counts
+    [S] int32 or None (device tensors)."""
+    import torch
+    m, l, o = state
+    _decode_checks(q, k_pool, v_pool, (tile_blocks, tile_block_counts, token_counts))
+    S, Hq, D = q.shape
+    _, BS, Hkv, _ = k_pool.shape
+    if m.shape != (S, Hq) or l.shape != (S, Hq) or o.shape != (S, Hq, D) or tile_blocks.dim() != 2:
+        raise ValueError("state must be ([S,Hq], [S,Hq], [S,Hq,D]) and tile_blocks [S,cap]")
+    need = rra_paged_decode_workspace_bytes(S, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rra_paged_decode_step(m, l, o, q, k_pool, v_pool, tile_blocks, tile_block_counts, token_counts, S, Hq, Hkv, D,
+                          BS, tile_blocks.shape[1], softmax_scale, workspace,
+                          workspace.numel() * workspace.element_size(), stream)
+    return state
+
+
+def paged_decode_finalize(state, out=None, stream=None):
+    """out = o / l (0 where l == 0), bf16 [S,Hq,D]."""
+    import torch
+    _, l, o = state
+    S, Hq, D = o.shape
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=o.device)
+    rra_paged_decode_finalize(l, o, out, S, Hq, D, stream)
     return out

@@ -49,19 +49,29 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int bs_shift)
 {
     return min(max(ctx, 0), max_blocks << bs_shift);
 }
+// Token count of sequence s (see CtxSource), clamped.
+__device__ __forceinline__ int ctx_of(const CtxSource &c, int s)
+{
+    if (c.context_lens) return clamp_ctx(c.context_lens[s], c.max_blocks, c.bs_shift);
+    const int nb = min(max(c.block_counts[s], 0), c.max_blocks);
+    const int full = nb << c.bs_shift;
+    return c.token_counts ? min(max(c.token_counts[s], 0), full) : full;
+}
+__host__ __device__ inline CtxSource ctx_source(const DecodeArgs &a)
+{
+    return CtxSource{a.context_lens, a.block_counts, a.token_counts, a.max_blocks, a.bs_shift};
+}
 
 // Group offsets goff[s] = sum_{s' < s} ceil(ctx_s' / 16), s = 0..S, into the
 // workspace (one workgroup).
-__global__ __launch_bounds__(256) void paged_decode_offsets_kernel(const int32_t *context_lens, int32_t num_seqs,
-                                                                   int32_t max_blocks, int32_t bs_shift,
-                                                                   int32_t *goff)
+__global__ __launch_bounds__(256) void paged_decode_offsets_kernel(CtxSource src, int32_t num_seqs, int32_t *goff)
 {
     __shared__ int wsum[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = 0;
     for (int base = 0; base < num_seqs; base += 256) {
         const int s = base + tid;
-        const int ctx = s < num_seqs ? clamp_ctx(context_lens[s], max_blocks, bs_shift) : 0;
+        const int ctx = s < num_seqs ? ctx_of(src, s) : 0;
         const int g = (ctx + kGroup - 1) / kGroup;
         int x = g;  // inclusive scan within the wave
         for (int off = 1; off < 64; off <<= 1) {
@@ -90,30 +100,25 @@ constexpr int kRegSeqs = 256;
 struct GroupOffsets {
     int incl[kRegSeqs / 64], ctxr[kRegSeqs / 64];
     const int32_t *mem;
-    const int32_t *ctx_mem;
-    int S, max_blocks, bs_shift;
+    CtxSource src;
+    int S;
     bool in_regs;
 
-    __device__ __forceinline__ void init(const int32_t *context_lens, const int32_t *goff_mem, int num_seqs,
-                                         int max_blocks_, int bs_shift_, int lane)
+    __device__ __forceinline__ void init(const CtxSource &src_, const int32_t *goff_mem, int num_seqs, int lane)
     {
         S = num_seqs;
         mem = goff_mem;
-        ctx_mem = context_lens;
-        max_blocks = max_blocks_;
-        bs_shift = bs_shift_;
+        src = src_;
         in_regs = S <= kRegSeqs;
         if (!in_regs) return;
-        int raw[kRegSeqs / 64];
 #pragma unroll
         for (int i = 0; i < kRegSeqs / 64; i++) {
             const int s = 64 * i + lane;
-            raw[i] = (64 * i < S && s < S) ? context_lens[s] : 0;
+            ctxr[i] = (64 * i < S && s < S) ? ctx_of(src, s) : 0;
         }
         int carry = 0;
 #pragma unroll
         for (int i = 0; i < kRegSeqs / 64; i++) {
-            ctxr[i] = clamp_ctx(raw[i], max_blocks, bs_shift);
             const int g = (ctxr[i] + kGroup - 1) / kGroup;
             int x = g;  // inclusive scan within the wave
             for (int off = 1; off < 64; off <<= 1) {
@@ -137,7 +142,7 @@ struct GroupOffsets {
     }
     __device__ __forceinline__ int ctx(int s) const
     {
-        return in_regs ? pick(ctxr, s >> 6, s & 63) : clamp_ctx(ctx_mem[s], max_blocks, bs_shift);
+        return in_regs ? pick(ctxr, s >> 6, s & 63) : ctx_of(src, s);
     }
     // first s in [0, S) with goff(s + 1) > g, for 0 <= g < goff(S)
     __device__ __forceinline__ int seq_of_group(int g, int lane) const
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     const int kh = unit / a.n_sub, sub = unit % a.n_sub;
     const int S = a.num_seqs;
     GroupOffsets go;
-    go.init(a.context_lens, a.ws_goff, S, a.max_blocks, a.bs_shift, lane);
+    go.init(ctx_source(a), a.ws_goff, S, lane);
     const int G = go.goff(S);
     const int P = G / a.n_ranges + (G % a.n_ranges != 0);  // groups per range
     const int64_t g_lo64 = (int64_t)blockIdx.x * P;
@@ -352,7 +357,9 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
 
 // Merge the pieces of each sequence and finalize: M = max m_c,
 // L = sum l_c 2^{(m_c - M) c}, O = sum o_c 2^{(m_c - M) c}, out = O / L
-// (0 when L == 0, i.e. an empty context).  One workgroup of NWC waves per
+// (0 when L == 0, i.e. an empty context).  A step of the stateful interface
+// merges the caller's state (m, l, o) in as one more piece (its m is in
+// scaled units) and stores the merged state instead of out.  One workgroup of NWC waves per
 // (sequence, q head): every wave finds M and L over all pieces (lane-parallel
 // loads), the waves split the o sums, and wave 0 adds their partial sums
 // from LDS.  A piece's o is D floats; LP = D/4 lanes read it as 16-byte
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     const int64_t pair = blockIdx.x;
     const int s = (int)(pair / a.num_q_heads), qh = (int)(pair % a.num_q_heads);
     GroupOffsets go;
-    go.init(a.context_lens, a.ws_goff, a.num_seqs, a.max_blocks, a.bs_shift, lane);
+    go.init(ctx_source(a), a.ws_goff, a.num_seqs, lane);
     const int G = go.goff(a.num_seqs);
     const int P = max(1, G / a.n_ranges + (G % a.n_ranges != 0));
     const int gs0 = go.goff(s), gs1 = go.goff(s + 1);
@@ -384,7 +391,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     float M = -INFINITY;
     for (int c = lane; c < npieces; c += 64) M = fmaxf(M, a.ws_m[slot(c)]);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float m_use = M == -INFINITY ? 0.f : M;
+    // stateful step: the caller's state is one more piece (m in scaled units)
+    const bool stateful = a.st_m != nullptr;
+    const float m_prev = stateful ? a.st_m[pair] : -INFINITY;
+    const float M_s = fmaxf(m_prev, M == -INFINITY ? -INFINITY : M * a.scale);  // merged max, scaled units
+    if (stateful && M_s == -INFINITY) return;  // nothing seen yet and nothing new (uniform in the workgroup)
+    const float m_use = stateful ? M_s / a.scale : (M == -INFINITY ? 0.f : M);
     float L = 0.f;
     f32x4 acc[NA];
 #pragma unroll
@@ -431,6 +443,20 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
         for (int w = 0; w < NWC - 1; w++)
 #pragma unroll
             for (int i = 0; i < NA; i++) acc[i] += *reinterpret_cast<const f32x4 *>(&part[w][4 * dl + 4 * LP * i]);
+        if (stateful) {
+            const float wp = m_prev == -INFINITY ? 0.f : fast_exp2((m_prev - M_s) * kLog2e);
+            float *so = a.st_o + pair * D + 4 * dl;
+#pragma unroll
+            for (int i = 0; i < NA; i++) {
+                f32x4 *p4 = reinterpret_cast<f32x4 *>(so + 4 * LP * i);
+                *p4 = acc[i] + wp * *p4;
+            }
+            if (dl == 0) {
+                a.st_l[pair] = L + wp * a.st_l[pair];
+                a.st_m[pair] = M_s;
+            }
+            return;
+        }
         const float inv = L > 0.f ? 1.f / L : 0.f;
         uint16_t *out = a.out + pair * D + 4 * dl;
 #pragma unroll
@@ -439,6 +465,55 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
             *reinterpret_cast<u32x2 *>(out + 4 * LP * i) = pr;
         }
     }
+}
+
+// finalize of the stateful interface: out = o / l, 0 where l == 0.  One
+// wave per (sequence, q head).
+__global__ __launch_bounds__(256) void decode_finalize_kernel(const float *state_l, const float *state_o,
+                                                              uint16_t *out, int64_t units, int32_t D)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= units) return;
+    const float l = state_l[u];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    for (int d = 4 * lane; d < D; d += 256) {
+        const f32x4 o = *reinterpret_cast<const f32x4 *>(state_o + u * D + d);
+        const u32x2 pr = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+        *reinterpret_cast<u32x2 *>(out + u * D + d) = pr;
+    }
+}
+
+// The stateful interface's initial state: m = -inf, l = 0, o = 0.
+__global__ __launch_bounds__(256) void decode_state_init_kernel(float *state_m, float *state_l, float *state_o,
+                                                                int64_t units, int32_t D)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < units) {
+        state_m[i] = -INFINITY;
+        state_l[i] = 0.f;
+    }
+    const int64_t n = units * D;
+    for (int64_t j = i; j < n; j += (int64_t)gridDim.x * 256) state_o[j] = 0.f;
+}
+
+hipError_t launch_decode_finalize(const float *state_l, const float *state_o, uint16_t *out, int64_t units,
+                                  int32_t head_dim, hipStream_t stream)
+{
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, state_l,
+                       state_o, out, units, head_dim);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_state_init(float *state_m, float *state_l, float *state_o, int64_t units, int32_t head_dim,
+                                    hipStream_t stream)
+{
+    if (units == 0) return hipSuccess;
+    const int64_t blocks = (units + 255) / 256;
+    hipLaunchKernelGGL(decode_state_init_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, state_m, state_l,
+                       state_o, units, head_dim);
+    return hipGetLastError();
 }
 
 // Test hook: the split kernel's address computation, as a plain copy.
@@ -484,8 +559,8 @@ template <int D>
 static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
 {
     if (a.num_seqs > kRegSeqs)
-        hipLaunchKernelGGL(paged_decode_offsets_kernel, dim3(1), dim3(256), 0, stream, a.context_lens, a.num_seqs,
-                           a.max_blocks, a.bs_shift, a.ws_goff);
+        hipLaunchKernelGGL(paged_decode_offsets_kernel, dim3(1), dim3(256), 0, stream, ctx_source(a), a.num_seqs,
+                           a.ws_goff);
     const int64_t units = (int64_t)a.num_kv_heads * a.n_sub;
     const dim3 grid((unsigned)a.n_ranges, (unsigned)((units + 3) / 4)), block(256);
     if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);

@@ -133,35 +133,34 @@ static int32_t log2_exact(int32_t x)
     return (1 << s) == x ? s : -1;
 }
 
-int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
-                              const int32_t *context_lens, void *out, int32_t num_seqs, int32_t num_q_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                              int32_t max_blocks_per_seq, float softmax_scale, void *workspace,
-                              size_t workspace_bytes, void *stream)
+// Checks and DecodeArgs set-up shared by the one-shot decode and the
+// stateful step: everything except the context source and the destination.
+static int32_t decode_setup(DecodeArgs &a, const void *q, const void *k_pool, const void *v_pool,
+                            const int32_t *block_table, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                            float softmax_scale, void *workspace, size_t workspace_bytes)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        max_blocks_per_seq < 0)
+        max_blocks < 0)
         return RRA_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads != 0) return RRA_ERR_INVALID_ARG;
     if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
     if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
     const int32_t bs_shift = log2_exact(block_size);
     if (bs_shift < 0 || block_size > 1024) return RRA_ERR_UNSUPPORTED;
-    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return RRA_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks * block_size > INT32_MAX) return RRA_ERR_INVALID_ARG;
     if ((int64_t)num_seqs * num_q_heads > INT32_MAX) return RRA_ERR_INVALID_ARG;  // one combine workgroup each
     if (num_seqs == 0) return RRA_OK;
-    if (!q || !out || !block_table || !context_lens) return RRA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return RRA_ERR_INVALID_ARG;
+    if (!q || !block_table) return RRA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return RRA_ERR_INVALID_ARG;
     const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RRA_ERR_WORKSPACE;
 
-    DecodeArgs a;
+    a = DecodeArgs{};
     a.q = static_cast<const uint16_t *>(q);
     a.k_pool = static_cast<const uint16_t *>(k_pool);
     a.v_pool = static_cast<const uint16_t *>(v_pool);
     a.block_table = block_table;
-    a.context_lens = context_lens;
-    a.out = static_cast<uint16_t *>(out);
     // workspace: goff [num_seqs + 1] int32 | m, l [slots * num_q_heads] fp32 |
     // o [slots * num_q_heads * head_dim] fp32, slots = n_ranges + num_seqs,
     // each part starting on a 256-byte boundary
@@ -179,12 +178,73 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.bs_shift = bs_shift;
-    a.max_blocks = max_blocks_per_seq;
+    a.max_blocks = max_blocks;
     a.n_ranges = n_ranges;
     const int32_t ratio = num_q_heads / num_kv_heads;
     a.n_sub = (ratio + 15) / 16;
+    a.scale = softmax_scale;
     a.scale_log2 = softmax_scale * kLog2e;
+    return RRA_OK;
+}
+
+int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                              const int32_t *context_lens, void *out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, float softmax_scale, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    DecodeArgs a;
+    const int32_t rc = decode_setup(a, q, k_pool, v_pool, block_table, num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, block_size, max_blocks_per_seq, softmax_scale, workspace,
+                                    workspace_bytes);
+    if (rc != RRA_OK || num_seqs == 0) return rc;
+    if (!context_lens || !out || !aligned16(out)) return RRA_ERR_INVALID_ARG;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint16_t *>(out);
     return hip_status(launch_paged_decode(a, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_paged_decode_step(float *state_m, float *state_l, float *state_o, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *tile_blocks, const int32_t *tile_block_counts,
+                              const int32_t *tile_token_counts, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t tile_capacity,
+                              float softmax_scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    DecodeArgs a;
+    const int32_t rc = decode_setup(a, q, k_pool, v_pool, tile_blocks, num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, block_size, tile_capacity, softmax_scale, workspace,
+                                    workspace_bytes);
+    if (rc != RRA_OK || num_seqs == 0) return rc;
+    if (!tile_block_counts || !state_m || !state_l || !state_o || !aligned16(state_o)) return RRA_ERR_INVALID_ARG;
+    a.block_counts = tile_block_counts;
+    a.token_counts = tile_token_counts;
+    a.st_m = state_m;
+    a.st_l = state_l;
+    a.st_o = state_o;
+    return hip_status(launch_paged_decode(a, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_paged_decode_finalize(const float *state_l, const float *state_o, void *out, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t head_dim, void *stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return RRA_OK;
+    if (!state_l || !state_o || !out || !aligned16(state_o) || !aligned16(out)) return RRA_ERR_INVALID_ARG;
+    return hip_status(launch_decode_finalize(state_l, state_o, static_cast<uint16_t *>(out),
+                                             (int64_t)num_seqs * num_q_heads, head_dim,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_paged_decode_state_init(float *state_m, float *state_l, float *state_o, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t head_dim, void *stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return RRA_OK;
+    if (!state_m || !state_l || !state_o) return RRA_ERR_INVALID_ARG;
+    return hip_status(launch_decode_state_init(state_m, state_l, state_o, (int64_t)num_seqs * num_q_heads,
+                                               head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int32_t rra_debug_paged_gather(const void *pool, const int32_t *block_table, const int32_t *context_lens,

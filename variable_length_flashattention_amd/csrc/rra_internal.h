@@ -40,9 +40,20 @@ hipError_t launch_varlen_tile_map(const int32_t *cu_q, const int32_t *cu_k, int3
                                   int32_t block_q, int32_t levels, int64_t n_items, int32_t *items_out,
                                   hipStream_t stream);
 
+// Where a sequence's token count comes from: context_lens[s] when given;
+// otherwise (a step of the stateful interface) block_counts[s] whole blocks,
+// cut at token_counts[s] when that is given.  Clamped to
+// [0, max_blocks * block_size] either way.
+struct CtxSource {
+    const int32_t *context_lens, *block_counts, *token_counts;
+    int32_t max_blocks, bs_shift;
+};
+
 struct DecodeArgs {
     const uint16_t *q, *k_pool, *v_pool;
     const int32_t *block_table, *context_lens;
+    const int32_t *block_counts, *token_counts;  // stateful step (context_lens null)
+    float *st_m, *st_l, *st_o;  // stateful step: the caller's state, merged in place
     uint16_t *out;
     int32_t *ws_goff;    // [num_seqs + 1] token-group offsets of the sequences
     float *ws_m, *ws_l, *ws_o;  // [n_ranges + num_seqs] x num_q_heads partial states
@@ -50,12 +61,17 @@ struct DecodeArgs {
     int32_t block_size, bs_shift, max_blocks;
     int32_t n_ranges;    // equal ranges of token groups, one wave each per kv head
     int32_t n_sub;       // q-head subgroups of 16 per kv head
-    float scale_log2;
+    float scale;         // softmax scale
+    float scale_log2;    // softmax scale * log2(e)
 };
 
 int32_t decode_n_ranges(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 hipError_t launch_paged_decode(const DecodeArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_finalize(const float *state_l, const float *state_o, uint16_t *out, int64_t units,
+                                  int32_t head_dim, hipStream_t stream);
+hipError_t launch_decode_state_init(float *state_m, float *state_l, float *state_o, int64_t units, int32_t head_dim,
+                                    hipStream_t stream);
 hipError_t launch_paged_gather(const uint16_t *pool, const int32_t *block_table, const int32_t *context_lens,
                                uint16_t *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                int32_t block_size, int32_t bs_shift, int32_t max_blocks, hipStream_t stream);
