@@ -9,6 +9,7 @@ from .oracle import (  # noqa: F401
     load,
     varlen_attn,
     varlen_attn_rows,
+    varlen_attn_paged,
     paged_decode,
     paged_decode_recurrent,
     decode_state_init,

@@ -124,7 +124,28 @@ typedef struct {
     /* sampled-row mode */
     const int32_t *rows; /* pairs (token, head) */
     int32_t Hkv;         /* kv heads; H % Hkv == 0 */
+    /* paged keys and values (block_table != NULL): k, v are pools
+     * [NB, BS, Hkv, D]; key j of sequence b is slot j % BS of pool block
+     * block_table[b, j / BS]; sequence b has seqlens_k[b] keys */
+    const int32_t *block_table, *seqlens_k;
+    int32_t BS, max_blocks;
 } varlen_ctx;
+
+/* Number of keys of sequence b. */
+static int64_t seq_keys(const varlen_ctx *c, int32_t b)
+{
+    return c->block_table ? (int64_t)c->seqlens_k[b] : (int64_t)c->cu_k[b + 1] - c->cu_k[b];
+}
+
+/* Row of kv head kh for key j of sequence b, in k or v (base).  Packed: token
+ * cu_k[b] + j of [total_k, Hkv, D].  Paged: the decode page's block-table
+ * addressing ([DECODE] step_tile_ref), applied to the keys of a prefill. */
+static const uint16_t *key_row(const varlen_ctx *c, const uint16_t *base, int32_t b, int64_t j, int64_t kh)
+{
+    if (!c->block_table) return base + (((int64_t)c->cu_k[b] + j) * c->Hkv + kh) * c->D;
+    const int64_t blk = c->block_table[(int64_t)b * c->max_blocks + j / c->BS];
+    return base + ((blk * c->BS + j % c->BS) * c->Hkv + kh) * c->D;
+}
 
 /* Is key j visible to query i?  Bottom-right causal alignment. */
 static int key_visible(int64_t i, int64_t j, int64_t Lq, int64_t Lk, int causal)
@@ -140,9 +161,9 @@ static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
 {
     const int64_t H = c->H, D = c->D, Hkv = c->Hkv;
     const int64_t kh = h / (H / Hkv);
-    const int64_t q0 = c->cu_q[b], k0 = c->cu_k[b];
+    const int64_t q0 = c->cu_q[b];
     const int64_t Lq = (int64_t)c->cu_q[b + 1] - q0;
-    const int64_t Lk = (int64_t)c->cu_k[b + 1] - k0;
+    const int64_t Lk = seq_keys(c, b);
     const uint16_t *qrow = c->q + ((q0 + i) * H + h) * D;
 
     /* scores of the visible keys, and their maximum */
@@ -150,7 +171,7 @@ static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
     int64_t n_visible = 0;
     for (int64_t j = 0; j < Lk; j++) {
         if (!key_visible(i, j, Lq, Lk, c->causal)) { scratch[j] = -INFINITY; continue; }
-        const uint16_t *krow = c->k + ((k0 + j) * Hkv + kh) * D;
+        const uint16_t *krow = key_row(c, c->k, b, j, kh);
         double dot = 0.0;
         for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(krow[d]);
         scratch[j] = c->scale * dot;
@@ -171,7 +192,7 @@ static void varlen_row(const varlen_ctx *c, int32_t b, int64_t i, int32_t h,
     for (int64_t j = 0; j < Lk; j++) {
         if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
         const double w = exp(scratch[j] - M) / Z;
-        const uint16_t *vrow = c->v + ((k0 + j) * Hkv + kh) * D;
+        const uint16_t *vrow = key_row(c, c->v, b, j, kh);
         for (int64_t d = 0; d < D; d++) out_row[d] += w * bf16_value(vrow[d]);
     }
     *lse_out = M + log(Z);
@@ -210,7 +231,8 @@ int oracle_varlen_attn_gqa(const uint16_t *q, const uint16_t *k, const uint16_t 
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
     for (int32_t b = 0; b < batch; b++)
         if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
-    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, NULL, num_kv_heads};
+    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, NULL, num_kv_heads,
+                    NULL, NULL, 0, 0};
     return run_units(varlen_unit, &c, (int64_t)batch * num_heads, (size_t)max_len(cu_k, batch), nthreads);
 }
 
@@ -247,7 +269,8 @@ int oracle_varlen_attn_rows_gqa(const uint16_t *q, const uint16_t *k, const uint
         if (rows[2 * r] < cu_q[0] || rows[2 * r] >= cu_q[batch]) return -1;
         if (rows[2 * r + 1] < 0 || rows[2 * r + 1] >= num_heads) return -1;
     }
-    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, rows, num_kv_heads};
+    varlen_ctx c = {q, k, v, cu_q, cu_k, batch, num_heads, head_dim, scale, causal, out, lse, rows, num_kv_heads,
+                    NULL, NULL, 0, 0};
     return run_units(varlen_sample_unit, &c, n_rows, (size_t)max_len(cu_k, batch), nthreads);
 }
 
@@ -259,6 +282,50 @@ int oracle_varlen_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t
 {
     return oracle_varlen_attn_rows_gqa(q, k, v, cu_q, cu_k, batch, num_heads, num_heads, head_dim, scale, causal,
                                        rows, n_rows, out, lse, nthreads);
+}
+
+/* Paged keys and values (chunked prefill): the same definition, with the
+ * keys and values of sequence b read through its block table as the decode
+ * page does ([DECODE] step_tile_ref), seqlens_k[b] of them.  With causal
+ * masking and Lk > Lq the queries are the last Lq positions of the sequence
+ * (bottom-right alignment above).  rows == NULL: every row; else the listed
+ * (packed query token, head) pairs, out/lse indexed by pair. */
+static int paged_check(const int32_t *cu_q, const int32_t *seqlens_k, const int32_t *block_table, int32_t batch,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t max_blocks)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks < 0) return -1;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
+    for (int32_t b = 0; b < batch; b++) {
+        if (cu_q[b + 1] < cu_q[b]) return -1;
+        if (seqlens_k[b] < 0 || (int64_t)seqlens_k[b] > (int64_t)max_blocks * block_size) return -1;
+        for (int64_t j = 0; j < ((int64_t)seqlens_k[b] + block_size - 1) / block_size; j++)
+            if (block_table[(int64_t)b * max_blocks + j] < 0) return -1;
+    }
+    return 0;
+}
+
+int oracle_varlen_attn_paged(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                             const int32_t *cu_q, const int32_t *seqlens_k, const int32_t *block_table,
+                             int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks, double scale, int32_t causal,
+                             const int32_t *rows, int64_t n_rows, double *out, double *lse, int32_t nthreads)
+{
+    if (paged_check(cu_q, seqlens_k, block_table, batch, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks))
+        return -1;
+    int64_t lk_max = 0;
+    for (int32_t b = 0; b < batch; b++)
+        if (seqlens_k[b] > lk_max) lk_max = seqlens_k[b];
+    varlen_ctx c = {q, k_pool, v_pool, cu_q, NULL, batch, num_heads, head_dim, scale, causal, out, lse, rows,
+                    num_kv_heads, block_table, seqlens_k, block_size, max_blocks};
+    if (!rows) return run_units(varlen_unit, &c, (int64_t)batch * num_heads, (size_t)lk_max, nthreads);
+    if (batch <= 0) return -1;
+    for (int64_t r = 0; r < n_rows; r++) {
+        if (rows[2 * r] < cu_q[0] || rows[2 * r] >= cu_q[batch]) return -1;
+        if (rows[2 * r + 1] < 0 || rows[2 * r + 1] >= num_heads) return -1;
+    }
+    return run_units(varlen_sample_unit, &c, n_rows, (size_t)lk_max, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -41,6 +41,9 @@ def _bind(lib):
     lib.oracle_varlen_attn_rows_gqa.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, f64, i32,
                                                 i32p, i64, f64p, f64p, i32]
     lib.oracle_varlen_attn_rows_gqa.restype = ctypes.c_int
+    lib.oracle_varlen_attn_paged.argtypes = [u16p, u16p, u16p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32,
+                                             f64, i32, ctypes.c_void_p, i64, f64p, f64p, i32]
+    lib.oracle_varlen_attn_paged.restype = ctypes.c_int
     lib.oracle_paged_decode.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32, f64, f64p, i32]
     lib.oracle_paged_decode.restype = ctypes.c_int
     lib.oracle_paged_decode_recurrent.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32,
@@ -116,6 +119,31 @@ def varlen_attn_rows(q, k, v, cu_q, cu_k, scale, causal, rows, nthreads=None, li
                                          nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_varlen_attn_rows rejected its arguments")
+    return out, lse
+
+
+def varlen_attn_paged(q, k_pool, v_pool, cu_q, seqlens_k, block_table, scale, causal, rows=None, nthreads=None,
+                      lib=None):
+    """Oracle with paged keys and values (chunked prefill): q [Tq,H,D]; pools
+    [NB,BS,Hkv,D]; seqlens_k [B] keys per sequence; block_table [B, maxb].
+    Returns (out [Tq,H,D], lse [Tq,H]), or with ``rows`` ([n, 2] of (packed
+    query token, head)) (out [n, D], lse [n])."""
+    lib = lib or load()
+    q, k_pool, v_pool = _c(q, np.uint16), _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    cu_q, lk, bt = _c(cu_q, np.int32), _c(seqlens_k, np.int32), _c(block_table, np.int32)
+    Tq, H, D = q.shape
+    _, BS, Hkv, _ = k_pool.shape
+    if rows is None:
+        out, lse, rp, n = np.full((Tq, H, D), np.nan), np.full((Tq, H), np.nan), None, 0
+    else:
+        rows = _c(rows, np.int32).reshape(-1, 2)
+        out, lse = np.full((rows.shape[0], D), np.nan), np.full((rows.shape[0],), np.nan)
+        rp, n = rows.ctypes.data_as(ctypes.c_void_p), rows.shape[0]
+    rc = lib.oracle_varlen_attn_paged(q, k_pool, v_pool, cu_q, lk, bt, len(cu_q) - 1, H, Hkv, D, BS, bt.shape[1],
+                                      float(scale), int(bool(causal)), rp, n, out, lse,
+                                      nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_varlen_attn_paged rejected its arguments")
     return out, lse
 
 

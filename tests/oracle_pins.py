@@ -18,7 +18,7 @@ from golden_cases import check as golden_check
 from golden_cases import golden_files
 from golden_cases import load as golden_load
 from variable_length_flashattention_amd.inputs import (bf16_bits, bf16_to_f32, cu_from_lengths, decode_case,
-                                                       varlen_case)
+                                                       paged_prefill_case, varlen_case)
 
 
 # --- an independent brute force ------------------------------------------------
@@ -261,6 +261,65 @@ def pin_gqa_prefill(lib):
                 f"gqa vs repeated heads, trial {trial}"
 
 
+def _gather_pool(pool, block_table, lengths):
+    """Packed [sum Lk, Hkv, D] rows of each sequence's keys, read from the pool
+    by numpy fancy indexing (token j of sequence b: slot j % BS of block
+    block_table[b, j // BS])."""
+    BS = pool.shape[1]
+    parts = []
+    for b, L in enumerate(lengths):
+        j = np.arange(int(L))
+        parts.append(pool[block_table[b, j // BS], j % BS])
+    return np.concatenate(parts) if parts else pool[:0, 0]
+
+
+def pin_paged_prefill(lib):
+    """Paged keys and values (chunked prefill).  (1) Equals the packed forward
+    pass on K/V gathered from the pool by numpy indexing, bit for bit, and the
+    brute force within 1e-12, over block sizes 1..16, GQA, Lk < Lq, Lk > Lq
+    and empty sequences; pool slots past the keys hold NaN and never leak.
+    (2) The bottom-right reading: a chunk holding the last Lq queries of a
+    sequence, with all L keys visible to it, gives exactly the rows L-Lq..L-1
+    of the causal self-attention over the whole sequence."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    for trial, (BS, H, Hkv) in enumerate([(1, 2, 2), (2, 4, 2), (4, 2, 1), (8, 3, 3), (16, 4, 4), (4, 6, 2)]):
+        B = int(rng.integers(1, 5))
+        lq = rng.integers(0, 10, size=B)
+        lk = rng.integers(0, 14, size=B)
+        c = paged_prefill_case("p", lq, lk, H, 8, BS, int(rng.integers(1 << 30)), True, num_kv_heads=Hkv,
+                               spare_blocks=int(rng.integers(0, 3)))
+        kg = _gather_pool(c.k_pool, c.block_table, c.seqlens_k)
+        vg = _gather_pool(c.v_pool, c.block_table, c.seqlens_k)
+        assert np.array_equal(kg, c.dense.k) and np.array_equal(vg, c.dense.v)  # the generator's own layout
+        cu_k = cu_from_lengths(c.seqlens_k)
+        for causal in (False, True):
+            o1, l1 = O.varlen_attn_paged(c.q, c.k_pool, c.v_pool, c.cu_q, c.seqlens_k, c.block_table, c.scale,
+                                         causal, lib=lib)
+            o2, l2 = O.varlen_attn(c.q, kg, vg, c.cu_q, cu_k, c.scale, causal, lib=lib)
+            assert np.array_equal(o1, o2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True), \
+                f"paged vs gathered, trial {trial} causal {causal}"
+            o3, l3 = brute_force_varlen(c.q, kg, vg, c.cu_q, cu_k, c.scale, causal)
+            _close(o1, o3, 1e-12, f"paged out trial {trial} causal {causal}")
+            _close(l1, l3, 1e-12, f"paged lse trial {trial} causal {causal}")
+            assert not np.any(np.isnan(o1)) and not np.any(np.isnan(l1)), f"NaN leaked, trial {trial}"
+            rows = np.array([[t, t % H] for t in range(int(c.cu_q[-1]))], dtype=np.int32).reshape(-1, 2)
+            if len(rows):
+                o4, l4 = O.varlen_attn_paged(c.q, c.k_pool, c.v_pool, c.cu_q, c.seqlens_k, c.block_table, c.scale,
+                                             causal, rows=rows, lib=lib)
+                assert np.array_equal(o4, o1[rows[:, 0], rows[:, 1]]) and \
+                    np.array_equal(l4, l1[rows[:, 0], rows[:, 1]]), f"paged sampled rows, trial {trial}"
+    # chunked prefill: the last Lq queries of each sequence against all L keys
+    L = [13, 7, 20]
+    chunk = [5, 7, 1]
+    full = paged_prefill_case("full", L, L, 2, 8, 4, 43, True)
+    of, lf = O.varlen_attn_paged(full.q, full.k_pool, full.v_pool, full.cu_q, full.seqlens_k, full.block_table,
+                                 full.scale, True, lib=lib)
+    sel = np.concatenate([np.arange(full.cu_q[b] + L[b] - chunk[b], full.cu_q[b + 1]) for b in range(3)])
+    oc, lc = O.varlen_attn_paged(full.q[sel], full.k_pool, full.v_pool, cu_from_lengths(chunk), full.seqlens_k,
+                                 full.block_table, full.scale, True, lib=lib)
+    assert np.array_equal(oc, of[sel]) and np.array_equal(lc, lf[sel]), "chunk rows differ from the full prefill"
+
+
 def pin_decode_direct_equals_recurrence(lib):
     """The direct softmax definition and the decode page's per-token (m, l, o)
     recurrence with state carried across tiles agree to fp64 rounding."""
@@ -442,6 +501,7 @@ ALL_PINS = [
     pin_scale_homogeneity,
     pin_sampled_rows_match_full,
     pin_gqa_prefill,
+    pin_paged_prefill,
     pin_decode_direct_equals_recurrence,
     pin_decode_equals_varlen_single_query,
     pin_decode_step,

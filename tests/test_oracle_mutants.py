@@ -22,10 +22,16 @@ MUTANTS = [
     ("lse_missing_max", "*lse_out = M + log(Z);", "*lse_out = log(Z);"),
     ("no_max_subtraction", "Z += exp(scratch[j] - M);", "Z += exp(scratch[j]);"),
     ("empty_row_lse_zero", "*lse_out = -INFINITY;\n        return;", "*lse_out = 0.0;\n        return;"),
-    ("key_head_ignored", "const uint16_t *krow = c->k + ((k0 + j) * Hkv + kh) * D;",
-     "const uint16_t *krow = c->k + ((k0 + j) * Hkv + 0) * D;"),
-    ("value_from_query_offset", "const uint16_t *vrow = c->v + ((k0 + j) * Hkv + kh) * D;",
-     "const uint16_t *vrow = c->v + ((q0 + j) * Hkv + kh) * D;"),
+    ("key_head_ignored", "+ j) * c->Hkv + kh) * c->D;", "+ j) * c->Hkv + 0) * c->D;"),
+    ("value_reads_keys", "const uint16_t *vrow = key_row(c, c->v, b, j, kh);",
+     "const uint16_t *vrow = key_row(c, c->k, b, j, kh);"),
+    ("packed_keys_at_query_offset", "(int64_t)c->cu_k[b] + j", "(int64_t)c->cu_q[b] + j"),
+    ("paged_slot_from_block", "return base + ((blk * c->BS + j % c->BS) * c->Hkv",
+     "return base + ((blk * c->BS + j / c->BS % c->BS) * c->Hkv"),
+    ("paged_table_row_ignored", "c->block_table[(int64_t)b * c->max_blocks + j / c->BS]", "c->block_table[j / c->BS]"),
+    ("paged_head_ignored", "c->BS) * c->Hkv + kh) * c->D;", "c->BS) * c->Hkv + 0) * c->D;"),
+    ("paged_one_key_short", "return c->block_table ? (int64_t)c->seqlens_k[b] :",
+     "return c->block_table ? (int64_t)c->seqlens_k[b] - 1 :"),
     ("gqa_prefill_interleaved", "const int64_t kh = h / (H / Hkv);", "const int64_t kh = h % Hkv;"),
     ("weights_not_normalised", "const double w = exp(scratch[j] - M) / Z;",
      "const double w = exp(scratch[j] - M);"),

@@ -136,6 +136,99 @@ def many_short(head_dim: int, causal: bool, seed: int | None = None) -> VarlenCa
 
 
 @dataclass
+class PagedPrefillCase:
+    """Forward-pass inputs with paged keys and values (chunked prefill):
+    q [Tq,H,D] packed by cu_q; k_pool/v_pool [NB,BS,Hkv,D]; sequence b has
+    seqlens_k[b] keys in pool blocks block_table[b, :ceil(Lk/BS)].  ``dense``
+    is the same data as a packed VarlenCase (k/v [Tk,Hkv,D] by cu_k)."""
+    name: str
+    q: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    cu_q: np.ndarray
+    seqlens_k: np.ndarray
+    block_table: np.ndarray
+    scale: float
+    causal: bool
+    seed: int
+    dense: VarlenCase
+    recipe: str = ""
+
+    @property
+    def batch(self) -> int:
+        return len(self.cu_q) - 1
+
+    @property
+    def num_heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_pool.shape[2]
+
+    @property
+    def head_dim(self) -> int:
+        return self.q.shape[2]
+
+    @property
+    def block_size(self) -> int:
+        return self.k_pool.shape[1]
+
+    @property
+    def max_blocks(self) -> int:
+        return self.block_table.shape[1]
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(np.max(np.diff(self.cu_q))) if self.batch else 0
+
+
+POOL_FILL = 0x7FC0  # bf16 NaN in pool slots past a sequence's last key
+
+
+def paged_prefill_case(name, lengths_q, lengths_k, num_heads, head_dim, block_size, seed, causal,
+                       num_kv_heads=None, q_mult=1.0, scale=None, max_blocks=None, spare_blocks=0,
+                       recipe="") -> PagedPrefillCase:
+    """Draws exactly what varlen_case draws (lengths, q, k, v), then a seeded
+    permutation of the pool blocks: sequence b's blocks are handed out in
+    order from the permutation.  Pool slots past the last key of a sequence,
+    and ``spare_blocks`` unused blocks, hold NaN, so a read of them shows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dense = varlen_case(name, lengths_q, lengths_k, num_heads, head_dim, seed, causal, q_mult=q_mult, scale=scale,
+                        rng=rng, recipe=recipe, num_kv_heads=num_kv_heads)
+    lk = np.asarray(lengths_k, dtype=np.int64)
+    nblk = (lk + block_size - 1) // block_size
+    NB = int(nblk.sum()) + spare_blocks
+    perm = rng.permutation(max(NB, 1)).astype(np.int32)
+    if max_blocks is None:
+        max_blocks = int(max(1, nblk.max() if len(nblk) else 1))
+    hkv = dense.num_kv_heads
+    k_pool = np.full((max(NB, 1), block_size, hkv, head_dim), POOL_FILL, dtype=np.uint16)
+    v_pool = np.full_like(k_pool, POOL_FILL)
+    bt = np.full((len(lk), max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+        j = np.arange(int(lk[b]))
+        k0 = int(dense.cu_k[b])
+        k_pool[bt[b, j // block_size], j % block_size] = dense.k[k0:k0 + len(j)]
+        v_pool[bt[b, j // block_size], j % block_size] = dense.v[k0:k0 + len(j)]
+    return PagedPrefillCase(name, dense.q, k_pool, v_pool, dense.cu_q, lk.astype(np.int32), bt, dense.scale,
+                            bool(causal), seed, dense, recipe)
+
+
+def chunked_paged(block_size: int = 16, seed: int = 3001, causal: bool = True) -> PagedPrefillCase:
+    """The skewed/chunked shape (q lengths {8192,1024,128,7}, k lengths
+    {8192,3072,128,519}, 16 heads, head_dim 128, bottom-right causal) with K/V
+    in a paged pool of ``block_size``-token blocks."""
+    return paged_prefill_case(f"chunked_paged_bs{block_size}", [8192, 1024, 128, 7], [8192, 3072, 128, 519], 16,
+                              128, block_size, seed, causal,
+                              recipe=f"Lq {{8192,1024,128,7}}, Lk {{8192,3072,128,519}}; H=16; D=128; "
+                                     f"K/V in {block_size}-token pool blocks, permuted table; bottom-right causal")
+
+
+@dataclass
 class DecodeCase:
     """Paged GQA decode inputs (bf16 bits + int32 tables)."""
     name: str
