@@ -87,6 +87,36 @@ int32_t rra_varlen_attn_fwd_gqa(const void *q, const void *k, const void *v, voi
                                 int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
                                 int32_t causal, void *stream);
 
+/*
+ * Paged keys and values (chunked prefill): the forward pass above with each
+ * sequence's keys and values read through a block table, with the paged
+ * layout of [DECODE] step_tile_ref, e.g. a prompt chunk attending to the
+ * context already in a paged KV cache.
+ *
+ *   q, out         bf16 [total_q, num_heads, head_dim], packed by cu_seqlens_q
+ *   lse            fp32 [total_q, num_heads]
+ *   k_pool, v_pool bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   cu_seqlens_q   int32 [batch + 1] device array (as above)
+ *   seqlens_k      int32 [batch] device array: keys of sequence b (Lk_b),
+ *                  clamped into [0, max_blocks_per_seq * block_size]
+ *   block_table    int32 [batch, max_blocks_per_seq] device array: key j of
+ *                  sequence b is slot j % block_size of pool block
+ *                  block_table[b, j / block_size]; entries at or past
+ *                  ceil(Lk_b / block_size) are never read
+ *   num_kv_heads   divides num_heads; query head h reads kv head
+ *                  h / (num_heads / num_kv_heads)
+ *   block_size     power of two in [8, 1024]
+ * Other arguments and results as for rra_varlen_attn_fwd; with causal = 1
+ * the mask is bottom-right aligned (query i of a sequence sees key j iff
+ * j <= i + Lk - Lq), so a chunk of the last Lq positions of a sequence sees
+ * its whole cached prefix.
+ */
+int32_t rra_varlen_attn_fwd_paged(const void *q, const void *k_pool, const void *v_pool, void *out, float *lse,
+                                  const int32_t *cu_seqlens_q, const int32_t *seqlens_k,
+                                  const int32_t *block_table, int32_t max_seqlen_q, int32_t batch,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, float softmax_scale, int32_t causal, void *stream);
+
 /* Query rows per work item of rra_varlen_attn_fwd for this head_dim and
  * max_seqlen_q (0 if head_dim is unsupported or max_seqlen_q < 0).  Work
  * items are (sequence, query tile, head). */

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ("rra_varlen_attn_fwd", "rra_varlen_attn_fwd_gqa", "rra_paged_decode_attn",
+    for n in ("rra_varlen_attn_fwd", "rra_varlen_attn_fwd_gqa", "rra_varlen_attn_fwd_paged", "rra_paged_decode_attn",
               "rra_paged_decode_workspace_bytes", "rra_paged_decode_state_init", "rra_paged_decode_step",
               "rra_paged_decode_finalize",
               "rra_status_string", "rra_varlen_block_q"):
@@ -98,6 +98,29 @@ def varlen_gqa_status(lib, **kw):
 ])
 def test_varlen_gqa_validation(lib, kw, status):
     assert varlen_gqa_status(lib, **kw) == status
+
+
+def paged_fwd_status(lib, **kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, out=FAKE, lse=FAKE, cuq=FAKE, lk=FAKE, bt=FAKE, maxq=16, batch=2, H=8, Hkv=2,
+             D=128, BS=16, MB=8, scale=0.1, causal=1)
+    a.update(kw)
+    return lib.rra_varlen_attn_fwd_paged(a["q"], a["kp"], a["vp"], a["out"], a["lse"], a["cuq"], a["lk"], a["bt"],
+                                         a["maxq"], a["batch"], a["H"], a["Hkv"], a["D"], a["BS"], a["MB"],
+                                         a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 1), (dict(H=0), 1), (dict(Hkv=3), 1), (dict(Hkv=0), 1), (dict(maxq=-1), 1), (dict(causal=3), 1),
+    (dict(scale=0.0), 1), (dict(BS=0), 1), (dict(MB=-1), 1), (dict(MB=1 << 28, BS=1024), 1),
+    (dict(D=96), 2), (dict(BS=4), 2), (dict(BS=24), 2), (dict(BS=2048), 2),
+    (dict(q=None), 1), (dict(out=None), 1), (dict(lse=None), 1), (dict(cuq=None), 1), (dict(lk=None), 1),
+    (dict(bt=None), 1), (dict(kp=None), 1), (dict(vp=FAKE + 2), 1), (dict(lse=FAKE + 2), 1),
+    (dict(batch=0), 0), (dict(maxq=0), 0), (dict(batch=0, q=None, bt=None), 0), (dict(BS=8), 0),
+])
+def test_varlen_paged_validation(lib, kw, status):
+    if status == 0 and kw.get("BS") == 8:
+        kw = dict(kw, maxq=0)  # accepted sizes, but nothing to launch here
+    assert paged_fwd_status(lib, **kw) == status
 
 
 def decode_status(lib, **kw):

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     rra_status_string,
     rra_varlen_attn_fwd,
     rra_varlen_attn_fwd_gqa,
+    rra_varlen_attn_fwd_paged,
     rra_varlen_block_q,
     rra_paged_decode_attn,
     rra_paged_decode_workspace_bytes,
@@ -20,6 +21,7 @@ from .binding import (  # noqa: F401
     rra_debug_varlen_tile_map,
     rra_debug_paged_gather,
     varlen_attn_fwd,
+    varlen_attn_fwd_paged,
     paged_decode_attn,
     decode_state_init,
     paged_decode_step,

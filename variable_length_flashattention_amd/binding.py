@@ -51,6 +51,9 @@ def load_library():
     lib.rra_varlen_attn_fwd.restype = i32
     lib.rra_varlen_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.rra_varlen_attn_fwd_gqa.restype = i32
+    lib.rra_varlen_attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                              f32, i32, vp]
+    lib.rra_varlen_attn_fwd_paged.restype = i32
     lib.rra_varlen_block_q.argtypes = [i32, i32]
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
@@ -118,6 +121,16 @@ def rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_s
         int(max_seqlen_q), int(batch), int(num_heads), int(num_kv_heads), int(head_dim), float(softmax_scale),
         int(bool(causal)), _stream(stream))
     _check("rra_varlen_attn_fwd_gqa", st)
+
+
+def rra_varlen_attn_fwd_paged(q, k_pool, v_pool, out, lse, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q, batch,
+                              num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, softmax_scale, causal,
+                              stream=None):
+    st = load_library().rra_varlen_attn_fwd_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(seqlens_k),
+        _ptr(block_table), int(max_seqlen_q), int(batch), int(num_heads), int(num_kv_heads), int(head_dim),
+        int(block_size), int(max_blocks_per_seq), float(softmax_scale), int(bool(causal)), _stream(stream))
+    _check("rra_varlen_attn_fwd_paged", st)
 
 
 def rra_paged_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
@@ -203,6 +216,27 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_s
         lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
     rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, cu_seqlens_q.numel() - 1,
                             H, k.shape[1], D, softmax_scale, causal, stream)
+    return out, lse
+
+
+def varlen_attn_fwd_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q, softmax_scale,
+                          causal, out=None, lse=None, stream=None):
+    """q [Tq,H,D] bf16 packed by cu_seqlens_q [B+1]; k_pool/v_pool
+    [NB,BS,Hkv,D] bf16; seqlens_k [B] and block_table [B,maxb] int32 (all
+    device tensors).  Returns (out bf16 [Tq,H,D], lse fp32 [Tq,H])."""
+    import torch
+    _decode_checks(q, k_pool, v_pool, (cu_seqlens_q, seqlens_k, block_table))
+    if q.shape[1] % k_pool.shape[2] != 0 or block_table.dim() != 2 or seqlens_k.numel() != cu_seqlens_q.numel() - 1 \
+            or block_table.shape[0] != seqlens_k.numel():
+        raise ValueError("bad shapes for a paged forward pass")
+    Tq, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
+    rra_varlen_attn_fwd_paged(q, k_pool, v_pool, out, lse, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q,
+                              seqlens_k.numel(), H, k_pool.shape[2], D, k_pool.shape[1], block_table.shape[1],
+                              softmax_scale, causal, stream)
     return out, lse
 
 

@@ -19,6 +19,14 @@ bool supported_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? RRA_OK : RRA_ERR_HIP; }
 
+// s with 2^s == x, or -1 if x is not a power of two in [1, 2^30]
+int32_t log2_exact(int32_t x)
+{
+    int32_t s = 0;
+    while (s < 30 && (1 << s) < x) s++;
+    return (1 << s) == x ? s : -1;
+}
+
 // Compute units of the current device (queried once per device).
 int device_cus()
 {
@@ -87,6 +95,57 @@ int32_t rra_varlen_attn_fwd_gqa(const void *q, const void *k, const void *v, voi
     a.n_items = (int64_t)batch * tiles_per_seq * num_heads;
     a.scale = softmax_scale;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.block_table = nullptr;
+    a.seqlens_k = nullptr;
+    a.bs_shift = 0;
+    a.max_blocks = 0;
+    return hip_status(launch_varlen_fwd(a, head_dim, causal == 1, device_cus(), static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_varlen_attn_fwd_paged(const void *q, const void *k_pool, const void *v_pool, void *out, float *lse,
+                                  const int32_t *cu_seqlens_q, const int32_t *seqlens_k,
+                                  const int32_t *block_table, int32_t max_seqlen_q, int32_t batch,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, float softmax_scale, int32_t causal, void *stream)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0 || max_seqlen_q < 0) return RRA_ERR_INVALID_ARG;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return RRA_ERR_INVALID_ARG;
+    if (block_size <= 0 || max_blocks_per_seq < 0) return RRA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return RRA_ERR_INVALID_ARG;
+    if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    const int32_t bs_shift = log2_exact(block_size);
+    if (bs_shift < 0 || block_size < 8 || block_size > 1024) return RRA_ERR_UNSUPPORTED;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return RRA_ERR_INVALID_ARG;
+    if (batch == 0 || max_seqlen_q == 0) return RRA_OK;  // no query rows exist
+    if (!q || !out || !lse || !cu_seqlens_q || !seqlens_k || !block_table || !k_pool || !v_pool)
+        return RRA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return RRA_ERR_INVALID_ARG;
+
+    VarlenArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k_pool);
+    a.v = static_cast<const uint16_t *>(v_pool);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = nullptr;
+    a.batch = batch;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.gqa_ratio = num_heads / num_kv_heads;
+    a.block_q = varlen_block_q(head_dim, max_seqlen_q);
+    const int64_t tiles_per_seq = ((int64_t)max_seqlen_q + a.block_q - 1) / a.block_q;
+    a.levels = (int32_t)tiles_per_seq;
+    a.n_items = (int64_t)batch * tiles_per_seq * num_heads;
+    a.scale = softmax_scale;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.block_table = block_table;
+    a.seqlens_k = seqlens_k;
+    a.bs_shift = bs_shift;
+    a.max_blocks = max_blocks_per_seq;
     return hip_status(launch_varlen_fwd(a, head_dim, causal == 1, device_cus(), static_cast<hipStream_t>(stream)));
 }
 
@@ -124,13 +183,6 @@ size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
     if (!supported_head_dim(head_dim)) return 0;
     return decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
-}
-
-static int32_t log2_exact(int32_t x)
-{
-    int32_t s = 0;
-    while ((1 << s) < x) s++;
-    return (1 << s) == x ? s : -1;
 }
 
 // Checks and DecodeArgs set-up shared by the one-shot decode and the

@@ -33,6 +33,11 @@ struct VarlenArgs {
     int64_t n_items;     // batch * levels * num_heads: upper bound on real items
     float scale;         // softmax scale
     float scale_log2;    // softmax scale * log2(e)
+    // paged keys and values (block_table != nullptr): k, v are pools
+    // [NB, BS, Hkv, D]; sequence b has seqlens_k[b] keys (clamped to
+    // [0, max_blocks * BS]) in blocks block_table[b * max_blocks + j]
+    const int32_t *block_table, *seqlens_k;
+    int32_t bs_shift, max_blocks;
 };
 
 hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream);

@@ -22,7 +22,9 @@ __device__ __forceinline__ int seq_tiles(const int32_t *__restrict__ cu, int b, 
 }
 
 // Tables one workgroup builds once in LDS and then decodes any number of
-// items from: cu_seqlens_q and _k copies, and G(x) for x = 0..levels.
+// items from: copies of cu_seqlens_q and of the key counts (nk ints: the
+// batch + 1 entries of cu_seqlens_k, or the batch entries of per-sequence
+// key counts), and G(x) for x = 0..levels.
 // They are used when 2*(batch+1) + levels + 1 fits the LDS space given;
 // otherwise items are decoded from global memory (decode_work_item_global).
 struct WorkTables {
@@ -34,7 +36,7 @@ struct WorkTables {
 // All threads of the workgroup call this; it ends with a barrier.  levels is
 // an upper bound on max_b n_b (ceil(max_seqlen_q / bq)).
 __device__ __forceinline__ WorkTables build_work_tables(const int32_t *__restrict__ cu_q,
-                                                        const int32_t *__restrict__ cu_k, int batch, int bq,
+                                                        const int32_t *__restrict__ cu_k, int nk, int batch, int bq,
                                                         int levels, int *lds, int lds_ints)
 {
     WorkTables t;
@@ -50,7 +52,7 @@ __device__ __forceinline__ WorkTables build_work_tables(const int32_t *__restric
     const int tid = threadIdx.x, nt = blockDim.x;
     for (int i = tid; i <= batch; i += nt) {
         t.cuq[i] = cu_q[i];
-        t.cuk[i] = cu_k[i];
+        if (i < nk) t.cuk[i] = cu_k[i];
     }
     for (int y = tid; y <= levels; y += nt) cnt[y] = 0;
     __syncthreads();

@@ -22,6 +22,14 @@
 // lane-local plus one permlane32 swap, and P^T feeds the second MMA straight
 // from the accumulator registers.  Key tiles past the last visible key of a
 // causal tile are never loaded.
+//
+// Paged keys and values (chunked prefill; PAGED): k and v are pools of
+// BS-token blocks and key j of sequence b is slot j % BS of block
+// block_table[b, j / BS], the addressing of step_tile_ref.  Each 1 KiB
+// direct-to-LDS load covers 1024 / (2D) consecutive keys, which lie in one
+// block when BS >= 8, so a load keeps one scalar buffer descriptor, based at
+// its first key's pool row; the table entries of a key tile are fetched
+// one per lane a tile ahead and picked with readlane.
 #include "rra_device.h"
 #include "rra_internal.h"
 #include "tile_map.h"
@@ -50,7 +58,7 @@ struct VarlenTile {
     static constexpr int MIN_BLOCKS = RPW == 1 ? (D == 64 ? 3 : D == 128 ? 2 : 1) : 1;
 };
 
-template <int D, bool CAUSAL, int RPW>
+template <int D, bool CAUSAL, bool PAGED, int RPW>
 __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>::MIN_BLOCKS)) void varlen_fwd_kernel(VarlenArgs a)
 {
     using T = VarlenTile<D, RPW>;
@@ -61,6 +69,9 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
     constexpr int NBUF = T::NBUF;
     constexpr int LOADS = 2 * T::WAVE_LOADS;  // direct-to-LDS loads per lane per key tile
     static_assert(NBUF >= 2 && NBUF <= 4, "buffer count");
+    // (paged: the table fetch issued with a tile's loads is covered by the
+    // full wait at the top of the next tile only when NBUF == 2)
+    static_assert(!PAGED || NBUF == 2, "paged staging assumes two buffers");
     // K and V tiles, NBUF buffers each, as distinct LDS objects: the compiler
     // then knows a read of one buffer does not depend on direct-to-LDS loads
     // still in flight into another, and does not wait for them.
@@ -78,7 +89,9 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.num_heads;
     const float sl2 = a.scale_log2;
-    const WorkTables wt = build_work_tables(a.cu_q, a.cu_k, a.batch, BQ, a.levels, sched, kSchedInts);
+    const int32_t *kcount = PAGED ? a.seqlens_k : a.cu_k;  // per-sequence key counts, or key offsets
+    const WorkTables wt = build_work_tables(a.cu_q, kcount, PAGED ? a.batch : a.batch + 1, a.batch, BQ, a.levels,
+                                            sched, kSchedInts);
 
     // persistent workgroups: items are dealt out in serpentine order
     for (int64_t k = 0;; k++) {
@@ -93,9 +106,17 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         b = __builtin_amdgcn_readfirstlane(b);
         qt = __builtin_amdgcn_readfirstlane(qt);
         h = __builtin_amdgcn_readfirstlane(h);
-        const int *cuq = wt.cached ? wt.cuq : a.cu_q, *cuk = wt.cached ? wt.cuk : a.cu_k;
-        const int q0 = __builtin_amdgcn_readfirstlane(cuq[b]), k0 = __builtin_amdgcn_readfirstlane(cuk[b]);
-        const int Lq = __builtin_amdgcn_readfirstlane(cuq[b + 1]) - q0, Lk = __builtin_amdgcn_readfirstlane(cuk[b + 1]) - k0;
+        const int *cuq = wt.cached ? wt.cuq : a.cu_q, *cuk = wt.cached ? wt.cuk : kcount;
+        const int q0 = __builtin_amdgcn_readfirstlane(cuq[b]);
+        const int Lq = __builtin_amdgcn_readfirstlane(cuq[b + 1]) - q0;
+        int k0, Lk;
+        if constexpr (PAGED) {
+            k0 = 0;
+            Lk = min(max(__builtin_amdgcn_readfirstlane(cuk[b]), 0), a.max_blocks << a.bs_shift);
+        } else {
+            k0 = __builtin_amdgcn_readfirstlane(cuk[b]);
+            Lk = __builtin_amdgcn_readfirstlane(cuk[b + 1]) - k0;
+        }
         const int diag = Lk - Lq;  // causal: key j visible to query i iff j <= i + diag
         const int i0 = qt * BQ;
         const int nrows = min(BQ, Lq - i0);
@@ -141,7 +162,47 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         const int kh = h / a.gqa_ratio;  // the kv head of query head h
         const uint8_t *kseq = reinterpret_cast<const uint8_t *>(a.k + ((int64_t)k0 * a.num_kv_heads + kh) * D);
         const uint8_t *vseq = reinterpret_cast<const uint8_t *>(a.v + ((int64_t)k0 * a.num_kv_heads + kh) * D);
-        auto stage = [&](int kt, uint8_t *kb, uint8_t *vb) {
+        // paged: a load's keys are rows lrow of a 1 KiB piece that starts at
+        // tile row (i*NW + wave) * RPB; the per-lane offsets hold lrow and
+        // the swizzled chunk, the descriptor the piece's first pool row
+        constexpr int RPB = 1024 / ROWB;
+        const int lrow = lane * 16 / ROWB;
+        uint32_t plane_k[NKO];
+#pragma unroll
+        for (int j = 0; j < NKO; j++)
+            plane_k[j] = (uint32_t)(lrow * row_bytes + 16 * (pch ^ T::swz_k(srow0 + j * RPL)));
+        const uint32_t plane_v = (uint32_t)(lrow * row_bytes + 16 * (pch ^ T::swz_v(srow0)));
+        const int32_t *table = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
+        const int last_blk = PAGED ? (Lk - 1) >> a.bs_shift : 0;
+        // lane j holds the table entry of block (tile's first block + j),
+        // clamped to the sequence's last block
+        auto fetch_table = [&](int kt) __attribute__((always_inline)) -> int {
+            return table[min(((kt * BK) >> a.bs_shift) + lane, last_blk)];
+        };
+        int tab = 0;
+        if (PAGED && Lk > 0) tab = fetch_table(0);
+        auto stage_paged = [&](int kt, uint8_t *kb, uint8_t *vb) __attribute__((always_inline)) {
+            const int kbase = kt * BK;
+            const int blk0 = kbase >> a.bs_shift;
+            const int cur = tab;
+            if (kt + 1 < nkt) tab = fetch_table(kt + 1);  // the next tile's, a tile ahead
+#pragma unroll
+            for (int i = 0; i < WL; i++) {
+                const int piece = i * NW + wave;
+                const int r = min(kbase + piece * RPB, Lk - 1);  // first key read (the last key past the end)
+                const int ent = __builtin_amdgcn_readlane(cur, (r >> a.bs_shift) - blk0);
+                const int64_t prow = ((int64_t)ent << a.bs_shift) + (r & ((1 << a.bs_shift) - 1));
+                const int64_t off = (prow * a.num_kv_heads + kh) * ROWB;
+                const __amdgpu_buffer_rsrc_t kr = raw_buffer(reinterpret_cast<const uint8_t *>(a.k) + off);
+                const __amdgpu_buffer_rsrc_t vr = raw_buffer(reinterpret_cast<const uint8_t *>(a.v) + off);
+                const int lim = Lk - 1 - r;  // keys of this piece past lim re-read key r + lim
+                const uint32_t back = lrow > lim ? (uint32_t)((lrow - lim) * row_bytes) : 0u;
+                const int blk = piece;
+                buffer_to_lds16(kr, kb + blk * 1024, plane_k[i % NKO] - back, 0);
+                buffer_to_lds16(vr, vb + blk * 1024, plane_v - back, 0);
+            }
+        };
+        auto stage_packed = [&](int kt, uint8_t *kb, uint8_t *vb) __attribute__((always_inline)) {
             const int64_t toff = (int64_t)kt * BK * row_bytes;
             const __amdgpu_buffer_rsrc_t kr = raw_buffer(kseq + toff), vr = raw_buffer(vseq + toff);
             if ((kt + 1) * BK <= Lk) {
@@ -162,6 +223,10 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                     buffer_to_lds16(vr, vb + blk * 1024, lane_v - back, i * RPL * row_bytes);
                 }
             }
+        };
+        auto stage = [&](int kt, uint8_t *kb, uint8_t *vb) {
+            if constexpr (PAGED) stage_paged(kt, kb, vb);
+            else stage_packed(kt, kb, vb);
         };
         if (nkt > 0) stage(0, k_lds0, v_lds0);
         if (NBUF > 2 && nkt > 1) stage(1, k_lds1, v_lds1);
@@ -383,7 +448,7 @@ __global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q
 {
     __shared__ int sched[kSchedInts];
     const int lane = threadIdx.x;
-    const WorkTables wt = build_work_tables(cu_q, cu_k, batch, block_q, levels, sched, kSchedInts);
+    const WorkTables wt = build_work_tables(cu_q, cu_k, batch + 1, batch, block_q, levels, sched, kSchedInts);
     for (int64_t w = blockIdx.x; w < n_items; w += gridDim.x) {
         int b = -1, qt = -1, h = -1;
         const bool ok = decode_work_item(wt, cu_q, num_heads, w, lane, b, qt, h);
@@ -401,11 +466,18 @@ static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStr
 {
     using T = VarlenTile<D, RPW>;
     if (a.block_q != T::BQ) return hipErrorInvalidValue;
+    // paged keys: one 1 KiB load's keys must lie in one block
+    if (a.block_table && (1 << a.bs_shift) * T::ROWB < 1024) return hipErrorInvalidValue;
     // persistent grid: as many workgroups as fit on the device at once
     const int64_t slots = (int64_t)num_cus * T::MIN_BLOCKS;
     const dim3 grid((unsigned)(a.n_items < slots ? a.n_items : slots)), block(T::THREADS);
-    if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, RPW>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, RPW>), grid, block, 0, stream, a);
+    if (a.block_table) {
+        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, true, RPW>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, true, RPW>), grid, block, 0, stream, a);
+    } else {
+        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, false, RPW>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, false, RPW>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
