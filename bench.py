@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="skip the context workloads")
     p.add_argument("--only", default="", choices=["", "mixed", "decode", "skewed", "many_short_d64",
-                                                  "many_short_d256"],
+                                                  "many_short_d256", "chunked_paged_bs16"],
                    help="time only this workload (for profiling runs)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run one plain device-to-device copy of BYTES bytes (a known-size reference "
@@ -108,6 +108,26 @@ class VarlenRun:
                                              c.scale, c.causal)
 
 
+class PagedRun:
+    """The forward pass with paged K/V (rra_varlen_attn_fwd_paged)."""
+    def __init__(self, torch, case):
+        import variable_length_flashattention_amd as rra
+        self.rra, self.case = rra, case
+        self.q = dev_bf16(torch, case.q)
+        self.kp, self.vp = dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)
+        self.cu_q = torch.from_numpy(case.cu_q).cuda()
+        self.lk = torch.from_numpy(case.seqlens_k).cuda()
+        self.bt = torch.from_numpy(case.block_table).cuda()
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        c = self.case
+        self.rra.rra_varlen_attn_fwd_paged(self.q, self.kp, self.vp, self.out, self.lse, self.cu_q, self.lk, self.bt,
+                                           c.max_seqlen_q, c.batch, c.num_heads, c.num_kv_heads, c.head_dim,
+                                           c.block_size, c.max_blocks, c.scale, c.causal)
+
+
 class DecodeRun:
     def __init__(self, torch, case):
         import variable_length_flashattention_amd as rra
@@ -126,6 +146,45 @@ class DecodeRun:
         self.rra.rra_paged_decode_attn(self.q, self.kp, self.vp, self.bt, self.cl, self.out, c.num_seqs,
                                        c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks,
                                        c.scale, self.ws, self.ws.numel())
+
+
+class DecodeStepsRun:
+    """The stateful decode on the decode workload: state init, the context of
+    every sequence folded in n_tiles consecutive tiles of blocks (one
+    rra_paged_decode_step each), then finalize."""
+    def __init__(self, torch, case, n_tiles=4):
+        import variable_length_flashattention_amd as rra
+        self.rra, self.case = rra, case
+        S, BS = case.num_seqs, case.block_size
+        self.q = dev_bf16(torch, case.q)
+        self.kp, self.vp = dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)
+        nblk = (case.context_lens.astype(np.int64) + BS - 1) // BS
+        cut = [np.minimum(nblk, (nblk * j + n_tiles - 1) // n_tiles) for j in range(n_tiles + 1)]
+        self.cap = max(1, max(int((cut[j + 1] - cut[j]).max()) for j in range(n_tiles)))
+        self.tiles = []
+        for j in range(n_tiles):
+            tb = np.full((S, self.cap), -1, dtype=np.int32)
+            cnt = (cut[j + 1] - cut[j]).astype(np.int32)
+            for s_ in range(S):
+                tb[s_, :cnt[s_]] = case.block_table[s_, cut[j][s_]:cut[j + 1][s_]]
+            tok = np.maximum(np.minimum(cut[j + 1] * BS, case.context_lens) - cut[j] * BS, 0).astype(np.int32)
+            self.tiles.append(tuple(torch.from_numpy(x).cuda() for x in (tb, cnt, tok)))
+        Hq, D = case.num_q_heads, case.head_dim
+        self.m = torch.empty((S, Hq), dtype=torch.float32, device="cuda")
+        self.l = torch.empty_like(self.m)
+        self.o = torch.empty((S, Hq, D), dtype=torch.float32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        need = rra.rra_paged_decode_workspace_bytes(S, Hq, case.num_kv_heads, D)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        c, r = self.case, self.rra
+        S, Hq, D = c.num_seqs, c.num_q_heads, c.head_dim
+        r.rra_paged_decode_state_init(self.m, self.l, self.o, S, Hq, D)
+        for tb, cnt, tok in self.tiles:
+            r.rra_paged_decode_step(self.m, self.l, self.o, self.q, self.kp, self.vp, tb, cnt, tok, S, Hq,
+                                    c.num_kv_heads, D, c.block_size, self.cap, c.scale, self.ws, self.ws.numel())
+        r.rra_paged_decode_finalize(self.l, self.o, self.out, S, Hq, D)
 
 
 def cpu_baseline(case, n_rows=131072, seed=7):
@@ -183,8 +242,12 @@ def main():
         del src, dst
     if args.only and args.only != "mixed":
         case = {"decode": None, "skewed": I.skewed(), "many_short_d64": I.many_short(64, True),
-                "many_short_d256": I.many_short(256, True)}[args.only]
-        if case is None:
+                "many_short_d256": I.many_short(256, True), "chunked_paged_bs16": "paged"}[args.only]
+        if case == "paged":
+            case = I.chunked_paged(16)
+            r = PagedRun(torch, case)
+            nbytes, flops = I.varlen_bytes(case.dense), I.varlen_flops(case.dense)
+        elif case is None:
             case = I.paged_decode()
             r = DecodeRun(torch, case)
             nbytes, flops = I.decode_bytes(case), I.decode_flops(case)
@@ -252,6 +315,14 @@ def main():
                        "context_tokens": int(dec.context_lens.sum()),
                        "note": "offsets + range + combine kernels per call; working set exceeds the 256 MiB MALL"}
     del drun
+    srun = DecodeStepsRun(torch, dec)
+    _, sper = time_launches(torch, srun, args.steps, args.warmup)
+    s_avg = float(np.mean(sper))
+    lines["decode"]["stateful_4_steps"] = {
+        "GB/s": round(dbytes / s_avg / 1e9, 1), "frac_of_hbm_peak": round(dbytes / s_avg / 1e9 / PEAK_HBM_GBS, 4),
+        "avg_us": round(s_avg * 1e6, 2),
+        "note": "state init + 4 rra_paged_decode_step calls (each context cut into 4 tiles of blocks) + finalize"}
+    del srun
     torch.cuda.empty_cache()
 
     if not args.quick:
@@ -259,16 +330,19 @@ def main():
         for name, case, bound in [
             ("tiny_causal", I.tiny(True), "latency"), ("tiny_noncausal", I.tiny(False), "latency"),
             ("skewed", I.skewed(), "mfma"),
+            ("chunked_paged_bs16", I.chunked_paged(16), "mfma"),
+            ("chunked_paged_bs256", I.chunked_paged(256), "mfma"),
             ("mixed_gqa_32q_8kv", I.mixed_gqa(), "mfma"),
             ("many_short_d64_causal", I.many_short(64, True), "hbm"),
             ("many_short_d64_noncausal", I.many_short(64, False), "hbm"),
             ("many_short_d256_causal", I.many_short(256, True), "hbm"),
             ("many_short_d256_noncausal", I.many_short(256, False), "hbm"),
         ]:
-            r = VarlenRun(torch, case)
+            r = PagedRun(torch, case) if isinstance(case, I.PagedPrefillCase) else VarlenRun(torch, case)
             _, p = time_launches(torch, r, 20, 3)
             t = float(np.mean(p))
-            f, b = I.varlen_flops(case), I.varlen_bytes(case)
+            dense = case.dense if isinstance(case, I.PagedPrefillCase) else case
+            f, b = I.varlen_flops(dense), I.varlen_bytes(dense)
             ctx[name] = {"avg_us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 2),
                          "frac_mfma_peak": round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "GB/s": round(b / t / 1e9, 1), "frac_hbm_peak": round(b / t / 1e9 / PEAK_HBM_GBS, 4),
