@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     varlen_attn,
     varlen_attn_rows,
     varlen_attn_paged,
+    varlen_attn_bwd,
     paged_decode,
     paged_decode_recurrent,
     decode_state_init,

@@ -329,6 +329,107 @@ int oracle_varlen_attn_paged(const uint16_t *q, const uint16_t *k_pool, const ui
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward pass of the packed forward pass (gradients of a scalar loss      */
+/* through out = softmax(scale q k^T + mask) v).  The pages name a backward  */
+/* module and keep lse for it without giving its arithmetic; this is the    */
+/* chain rule of the definition above, nothing more:                        */
+/*   P_ij  = exp(s_ij - lse_i)            (the forward's probabilities)     */
+/*   dV_j  = sum_i P_ij dO_i                                                */
+/*   dP_ij = dO_i . v_j                                                     */
+/*   dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')   (softmax Jacobian)        */
+/*   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i          */
+/* over the visible pairs (i, j) of one (sequence, query head); with        */
+/* grouped-query K/V the kv head's dK and dV sum over its query heads.      */
+/* Everything is recomputed in double from the bf16 inputs (out and lse of  */
+/* the forward are not inputs here).  A row with no visible key has zero    */
+/* gradient; keys that no query sees get dK = dV = 0.                       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    const int32_t *cu_q, *cu_k;
+    int32_t H, Hkv, D;
+    double scale;
+    int32_t causal;
+    double *dq, *dk, *dv;
+} bwd_ctx;
+
+/* unit = b*Hkv + kh: every query head of kv head kh, every row of sequence b
+ * (the units write disjoint rows of dq, dk, dv).  scratch: 2*Lk doubles. */
+static void bwd_unit(void *p, int64_t unit, double *scratch)
+{
+    const bwd_ctx *c = (const bwd_ctx *)p;
+    const int32_t b = (int32_t)(unit / c->Hkv), kh = (int32_t)(unit % c->Hkv);
+    const int64_t H = c->H, Hkv = c->Hkv, D = c->D, R = H / Hkv;
+    const int64_t q0 = c->cu_q[b], k0 = c->cu_k[b];
+    const int64_t Lq = (int64_t)c->cu_q[b + 1] - q0, Lk = (int64_t)c->cu_k[b + 1] - k0;
+    double *prob = scratch, *dprob = scratch + Lk;
+    for (int64_t j = 0; j < Lk; j++)
+        for (int64_t d = 0; d < D; d++) {
+            c->dk[((k0 + j) * Hkv + kh) * D + d] = 0.0;
+            c->dv[((k0 + j) * Hkv + kh) * D + d] = 0.0;
+        }
+    for (int64_t h = kh * R; h < (kh + 1) * R; h++)
+        for (int64_t i = 0; i < Lq; i++) {
+            const uint16_t *qrow = c->q + ((q0 + i) * H + h) * D;
+            const uint16_t *dorow = c->dout + ((q0 + i) * H + h) * D;
+            double *dqrow = c->dq + ((q0 + i) * H + h) * D;
+            for (int64_t d = 0; d < D; d++) dqrow[d] = 0.0;
+            /* probabilities of the row (the forward's softmax) */
+            double M = -INFINITY;
+            for (int64_t j = 0; j < Lk; j++) {
+                prob[j] = -INFINITY;
+                if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
+                const uint16_t *krow = c->k + ((k0 + j) * Hkv + kh) * D;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(krow[d]);
+                prob[j] = c->scale * dot;
+                if (prob[j] > M) M = prob[j];
+            }
+            if (M == -INFINITY) continue; /* no visible key */
+            double Z = 0.0;
+            for (int64_t j = 0; j < Lk; j++)
+                if (prob[j] != -INFINITY) Z += exp(prob[j] - M);
+            for (int64_t j = 0; j < Lk; j++) prob[j] = prob[j] == -INFINITY ? 0.0 : exp(prob[j] - M) / Z;
+            /* dP and the row's sum_j P_ij dP_ij */
+            double rowdot = 0.0;
+            for (int64_t j = 0; j < Lk; j++) {
+                dprob[j] = 0.0;
+                if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
+                const uint16_t *vrow = c->v + ((k0 + j) * Hkv + kh) * D;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; d++) dot += bf16_value(dorow[d]) * bf16_value(vrow[d]);
+                dprob[j] = dot;
+                rowdot += prob[j] * dot;
+            }
+            for (int64_t j = 0; j < Lk; j++) {
+                if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
+                const double ds = prob[j] * (dprob[j] - rowdot);
+                const uint16_t *krow = c->k + ((k0 + j) * Hkv + kh) * D;
+                double *dkrow = c->dk + ((k0 + j) * Hkv + kh) * D;
+                double *dvrow = c->dv + ((k0 + j) * Hkv + kh) * D;
+                for (int64_t d = 0; d < D; d++) {
+                    dvrow[d] += prob[j] * bf16_value(dorow[d]);
+                    dqrow[d] += c->scale * ds * bf16_value(krow[d]);
+                    dkrow[d] += c->scale * ds * bf16_value(qrow[d]);
+                }
+            }
+        }
+}
+
+int oracle_varlen_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                           const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, double scale, int32_t causal,
+                           double *dq, double *dk, double *dv, int32_t nthreads)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0) return -1;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
+    for (int32_t b = 0; b < batch; b++)
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
+    bwd_ctx c = {q, k, v, dout, cu_q, cu_k, num_heads, num_kv_heads, head_dim, scale, causal, dq, dk, dv};
+    return run_units(bwd_unit, &c, (int64_t)batch * num_kv_heads, 2 * (size_t)max_len(cu_k, batch) + 1, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Paged-KV GQA decode.                                                     */
 /*                                                                          */
 /* [DECODE] layout: q, out [S, Hq, D]; k_pool, v_pool [NB, BS, Hkv, D];     */

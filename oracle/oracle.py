@@ -44,6 +44,9 @@ def _bind(lib):
     lib.oracle_varlen_attn_paged.argtypes = [u16p, u16p, u16p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32,
                                              f64, i32, ctypes.c_void_p, i64, f64p, f64p, i32]
     lib.oracle_varlen_attn_paged.restype = ctypes.c_int
+    lib.oracle_varlen_attn_bwd.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, f64, i32, f64p,
+                                           f64p, f64p, i32]
+    lib.oracle_varlen_attn_bwd.restype = ctypes.c_int
     lib.oracle_paged_decode.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32, f64, f64p, i32]
     lib.oracle_paged_decode.restype = ctypes.c_int
     lib.oracle_paged_decode_recurrent.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32,
@@ -145,6 +148,25 @@ def varlen_attn_paged(q, k_pool, v_pool, cu_q, seqlens_k, block_table, scale, ca
     if rc != 0:
         raise ValueError("oracle_varlen_attn_paged rejected its arguments")
     return out, lse
+
+
+def varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, scale, causal, nthreads=None, lib=None):
+    """Gradients of sum(out * dout) of the packed forward pass: q, dout
+    [Tq,H,D], k, v [Tk,Hkv,D] bf16 bits.  Returns (dq [Tq,H,D], dk [Tk,Hkv,D],
+    dv [Tk,Hkv,D]) float64; rows outside every sequence stay NaN."""
+    lib = lib or load()
+    q, k, v, dout = (_c(x, np.uint16) for x in (q, k, v, dout))
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    Tq, H, D = q.shape
+    Tk, Hkv, _ = k.shape
+    dq = np.full((Tq, H, D), np.nan)
+    dk = np.full((Tk, Hkv, D), np.nan)
+    dv = np.full((Tk, Hkv, D), np.nan)
+    rc = lib.oracle_varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, len(cu_q) - 1, H, Hkv, D, float(scale),
+                                    int(bool(causal)), dq, dk, dv, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_varlen_attn_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def _decode_args(q, k_pool, v_pool, block_table, context_lens):

@@ -320,6 +320,114 @@ def pin_paged_prefill(lib):
     assert np.array_equal(oc, of[sel]) and np.array_equal(lc, lf[sel]), "chunk rows differ from the full prefill"
 
 
+def _torch_attention_grads(q, k, v, dout, cu_q, cu_k, scale, causal):
+    """dq, dk, dv by torch autograd (CPU, float64) of a dense masked softmax
+    attention per sequence; kv head h // (H // Hkv) via repeat_interleave."""
+    import torch
+    qf, kf, vf, gf = (torch.from_numpy(bf16_to_f32(x).astype(np.float64)) for x in (q, k, v, dout))
+    qf.requires_grad_(True)
+    kf.requires_grad_(True)
+    vf.requires_grad_(True)
+    R = qf.shape[1] // kf.shape[1]
+    loss = torch.zeros((), dtype=torch.float64)
+    for b in range(len(cu_q) - 1):
+        qs, ks, vs = qf[cu_q[b]:cu_q[b + 1]], kf[cu_k[b]:cu_k[b + 1]], vf[cu_k[b]:cu_k[b + 1]]
+        Lq, Lk = qs.shape[0], ks.shape[0]
+        if Lq == 0 or Lk == 0:
+            continue
+        kr = ks.repeat_interleave(R, dim=1).transpose(0, 1)    # [H, Lk, D]
+        vr = vs.repeat_interleave(R, dim=1).transpose(0, 1)
+        s = scale * torch.matmul(qs.transpose(0, 1), kr.transpose(1, 2))  # [H, Lq, Lk]
+        i = torch.arange(Lq)[:, None]
+        j = torch.arange(Lk)[None, :]
+        vis = (j <= i + Lk - Lq) if causal else torch.ones(Lq, Lk, dtype=torch.bool)
+        s = s.masked_fill(~vis, float("-inf"))
+        has = vis.any(dim=1)                                     # rows with a visible key
+        p = torch.softmax(s[:, has], dim=-1)
+        o = torch.matmul(p, vr)                                  # [H, rows, D]
+        loss = loss + (o * gf[cu_q[b]:cu_q[b + 1]].transpose(0, 1)[:, has]).sum()
+    loss.backward()
+    z = lambda t: t.grad.numpy() if t.grad is not None else np.zeros(t.shape)
+    return z(qf), z(kf), z(vf)
+
+
+def _f64_forward_loss(qf, kf, vf, gf, cu_q, cu_k, scale, causal):
+    """sum(out * dout) of the forward definition on float64 inputs (numpy)."""
+    R = qf.shape[1] // kf.shape[1]
+    total = 0.0
+    for b in range(len(cu_q) - 1):
+        Lq, Lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for i in range(Lq):
+            for h in range(qf.shape[1]):
+                js = [j for j in range(Lk) if not causal or j <= i + Lk - Lq]
+                if not js:
+                    continue
+                x = np.array([scale * np.dot(qf[cu_q[b] + i, h], kf[cu_k[b] + j, h // R]) for j in js])
+                w = np.exp(x - x.max())
+                w /= w.sum()
+                o = sum(wj * vf[cu_k[b] + j, h // R] for wj, j in zip(w, js))
+                total += float(np.dot(o, gf[cu_q[b] + i, h]))
+    return total
+
+
+def pin_backward(lib):
+    """Gradients of sum(out * dout): (1) equal torch autograd of a dense masked
+    softmax attention (float64, CPU) within 1e-10 over empty sequences,
+    Lk < Lq, Lk > Lq, both causal modes and grouped-query K/V; (2) equal
+    central finite differences of the float64 forward definition; (3) the
+    closed forms sum_j dK_j = 0 (softmax rows sum to one, so the dS rows sum
+    to zero) and sum_j dV_j = sum of dO over rows with a visible key, per
+    (sequence, kv head)."""
+    rng = np.random.Generator(np.random.PCG64(51))
+    for trial, (H, Hkv) in enumerate([(2, 2), (4, 2), (3, 1), (2, 2), (4, 4)]):
+        c = _random_case(rng, B=int(rng.integers(1, 4)), H=H, D=8, max_len=8, Hkv=Hkv)
+        dout = normal_bf16_like(rng, c.q.shape)
+        for causal in (False, True):
+            dq, dk, dv = O.varlen_attn_bwd(c.q, c.k, c.v, dout, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+            tq, tk, tv = _torch_attention_grads(c.q, c.k, c.v, dout, c.cu_q, c.cu_k, c.scale, causal)
+            _close(dq, tq, 1e-10, f"dq trial {trial} causal {causal}")
+            _close(dk, tk, 1e-10, f"dk trial {trial} causal {causal}")
+            _close(dv, tv, 1e-10, f"dv trial {trial} causal {causal}")
+            gf = bf16_to_f32(dout).astype(np.float64)
+            R = H // Hkv
+            for b in range(c.batch):
+                ks, ke = c.cu_k[b], c.cu_k[b + 1]
+                if ke == ks:
+                    continue
+                Lq, Lk = c.cu_q[b + 1] - c.cu_q[b], ke - ks
+                assert np.all(np.abs(dk[ks:ke].sum(axis=0)) <= 1e-12 * (1 + np.abs(dk[ks:ke]).sum(axis=0))), \
+                    f"sum of dK, trial {trial}"
+                for kh in range(Hkv):
+                    want = np.zeros(c.head_dim)
+                    for i in range(Lq):
+                        if not causal or i + Lk - Lq >= 0:
+                            want += gf[c.cu_q[b] + i, kh * R:(kh + 1) * R].sum(axis=0)
+                    _close(dv[ks:ke, kh].sum(axis=0), want, 1e-12, f"sum of dV, trial {trial}")
+    # finite differences on one small case
+    c = _random_case(np.random.Generator(np.random.PCG64(52)), B=2, H=2, D=4, max_len=5, Hkv=1)
+    dout = normal_bf16_like(rng, c.q.shape)
+    qf, kf, vf, gf = (bf16_to_f32(x).astype(np.float64) for x in (c.q, c.k, c.v, dout))
+    for causal in (False, True):
+        grads = O.varlen_attn_bwd(c.q, c.k, c.v, dout, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+        for which, (arr, g) in enumerate(zip((qf, kf, vf), grads)):
+            if arr.shape[0] == 0:
+                continue
+            for _ in range(4):
+                idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+                eps = 1e-6
+                arr[idx] += eps
+                up = _f64_forward_loss(qf, kf, vf, gf, c.cu_q, c.cu_k, c.scale, causal)
+                arr[idx] -= 2 * eps
+                dn = _f64_forward_loss(qf, kf, vf, gf, c.cu_q, c.cu_k, c.scale, causal)
+                arr[idx] += eps
+                fd = (up - dn) / (2 * eps)
+                assert abs(fd - g[idx]) <= 1e-6 * (1 + abs(fd)), f"finite difference {which} {idx}: {fd} vs {g[idx]}"
+
+
+def normal_bf16_like(rng, shape):
+    return bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
+
+
 def pin_decode_direct_equals_recurrence(lib):
     """The direct softmax definition and the decode page's per-token (m, l, o)
     recurrence with state carried across tiles agree to fp64 rounding."""
@@ -502,6 +610,7 @@ ALL_PINS = [
     pin_sampled_rows_match_full,
     pin_gqa_prefill,
     pin_paged_prefill,
+    pin_backward,
     pin_decode_direct_equals_recurrence,
     pin_decode_equals_varlen_single_query,
     pin_decode_step,

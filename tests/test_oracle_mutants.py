@@ -46,6 +46,16 @@ MUTANTS = [
      "const double inv_l = 1.0 / state_l[u];"),
     ("step_state_not_carried", "double m = c->m[unit], l = c->l[unit];", "double m = -INFINITY, l = 0.0;"),
     ("finalize_unguarded", "const double inv_l = st_l > 0.0 ? 1.0 / st_l : 0.0;", "const double inv_l = 1.0 / st_l;"),
+    ("bwd_jacobian_without_rowdot", "const double ds = prob[j] * (dprob[j] - rowdot);",
+     "const double ds = prob[j] * dprob[j];"),
+    ("bwd_dk_unscaled", "dkrow[d] += c->scale * ds * bf16_value(qrow[d]);", "dkrow[d] += ds * bf16_value(qrow[d]);"),
+    ("bwd_dv_from_ds", "dvrow[d] += prob[j] * bf16_value(dorow[d]);", "dvrow[d] += ds * bf16_value(dorow[d]);"),
+    ("bwd_dq_from_values", "dqrow[d] += c->scale * ds * bf16_value(krow[d]);",
+     "dqrow[d] += c->scale * ds * bf16_value(c->v[((k0 + j) * Hkv + kh) * D + d]);"),
+    ("bwd_group_first_head_only", "for (int64_t h = kh * R; h < (kh + 1) * R; h++)",
+     "for (int64_t h = kh * R; h < kh * R + 1; h++)"),
+    ("bwd_unnormalised_probs", "prob[j] = prob[j] == -INFINITY ? 0.0 : exp(prob[j] - M) / Z;",
+     "prob[j] = prob[j] == -INFINITY ? 0.0 : exp(prob[j] - M);"),
     ("tile_levels_ascending", "for (int64_t r = max_tiles - 1; r >= 0; r--) {", "for (int64_t r = 0; r < max_tiles; r++) {"),
     ("tile_count_floor", "const int64_t n = (L + block_q - 1) / block_q;\n            if (n <= r) continue;",
      "const int64_t n = L / block_q;\n            if (n <= r) continue;"),
