@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="skip the context workloads")
     p.add_argument("--only", default="", choices=["", "mixed", "decode", "skewed", "many_short_d64",
-                                                  "many_short_d256", "chunked_paged_bs16"],
+                                                  "many_short_d256", "chunked_paged_bs16", "backward"],
                    help="time only this workload (for profiling runs)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run one plain device-to-device copy of BYTES bytes (a known-size reference "
@@ -106,6 +106,37 @@ class VarlenRun:
             self.rra.rra_varlen_attn_fwd_gqa(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
                                              c.max_seqlen_q, c.batch, c.num_heads, c.num_kv_heads, c.head_dim,
                                              c.scale, c.causal)
+
+
+class BwdRun:
+    """The backward pass (rra_varlen_attn_bwd) on the forward's out and lse
+    for a fixed upstream gradient."""
+    def __init__(self, torch, case, seed=2002):
+        import variable_length_flashattention_amd as rra
+        self.rra, self.case = rra, case
+        self.q, self.k, self.v = dev_bf16(torch, case.q), dev_bf16(torch, case.k), dev_bf16(torch, case.v)
+        self.cu_q = torch.from_numpy(case.cu_q).cuda()
+        self.cu_k = torch.from_numpy(case.cu_k).cuda()
+        self.dout = dev_bf16(torch, I_normal(case.q.shape, seed))
+        self.out, self.lse = rra.varlen_attn_fwd(self.q, self.k, self.v, self.cu_q, self.cu_k, case.max_seqlen_q,
+                                                 case.scale, case.causal)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.tq = int(case.cu_q[-1])
+        self.max_k = int(np.max(np.diff(case.cu_k)))
+        need = rra.rra_varlen_attn_bwd_workspace_bytes(self.tq, case.num_heads)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        c = self.case
+        self.rra.rra_varlen_attn_bwd(self.q, self.k, self.v, self.out, self.lse, self.dout, self.dq, self.dk,
+                                     self.dv, self.cu_q, self.cu_k, self.tq, c.max_seqlen_q, self.max_k, c.batch,
+                                     c.num_heads, c.num_kv_heads, c.head_dim, c.scale, c.causal, self.ws,
+                                     self.ws.numel())
+
+
+def I_normal(shape, seed):
+    from variable_length_flashattention_amd import inputs as I
+    return I.normal_bf16(np.random.Generator(np.random.PCG64(seed)), shape)
 
 
 class PagedRun:
@@ -242,8 +273,13 @@ def main():
         del src, dst
     if args.only and args.only != "mixed":
         case = {"decode": None, "skewed": I.skewed(), "many_short_d64": I.many_short(64, True),
-                "many_short_d256": I.many_short(256, True), "chunked_paged_bs16": "paged"}[args.only]
-        if case == "paged":
+                "many_short_d256": I.many_short(256, True), "chunked_paged_bs16": "paged",
+                "backward": "backward"}[args.only]
+        if case == "backward":
+            case = I.mixed()
+            r = BwdRun(torch, case)
+            nbytes, flops = 2 * I.varlen_bytes(case), int(2.5 * I.varlen_flops(case))
+        elif case == "paged":
             case = I.chunked_paged(16)
             r = PagedRun(torch, case)
             nbytes, flops = I.varlen_bytes(case.dense), I.varlen_flops(case.dense)
@@ -323,6 +359,19 @@ def main():
         "avg_us": round(s_avg * 1e6, 2),
         "note": "state init + 4 rra_paged_decode_step calls (each context cut into 4 tiles of blocks) + finalize"}
     del srun
+    torch.cuda.empty_cache()
+
+    # backward of the mixed workload (5 matmuls' worth of algorithmic flops:
+    # 2.5x the forward's)
+    brun = BwdRun(torch, mixed)
+    _, bper = time_launches(torch, brun, args.steps, args.warmup)
+    b_avg = float(np.mean(bper))
+    lines["backward"] = {"workload": "backward of the mixed workload (dq, dk, dv from out, lse, dout)",
+                         "TFLOP/s": round(2.5 * flops / b_avg / 1e12, 2),
+                         "frac_mfma_peak": round(2.5 * flops / b_avg / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "avg_call_us": round(b_avg * 1e6, 2),
+                         "note": "prep + dq + dk/dv kernels per call; flops = 2.5 x forward (S, dP, dV, dK, dQ)"}
+    del brun
     torch.cuda.empty_cache()
 
     if not args.quick:

@@ -117,6 +117,42 @@ int32_t rra_varlen_attn_fwd_paged(const void *q, const void *k_pool, const void 
                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                   int32_t max_blocks_per_seq, float softmax_scale, int32_t causal, void *stream);
 
+/*
+ * Backward pass of rra_varlen_attn_fwd / _gqa: the gradients of a loss L
+ * with respect to q, k and v, given dout = dL/dout.  The plan names a
+ * backward module and keeps lse for it ([PLAN] Task 1, "Write output and
+ * LSE") without defining it further; this is the chain rule of the forward
+ * definition: with P_ij = exp(scale q_i.k_j - lse_i) over the visible pairs,
+ *   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (dout_i.v_j - dout_i.out_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i
+ * (grouped-query: dk, dv of a kv head sum over its query heads).
+ *
+ *   q, out, dout, dq  bf16 [total_q, num_heads, head_dim]
+ *   k, v, dk, dv      bf16 [total_k, num_kv_heads, head_dim]
+ *   lse               fp32 [total_q, num_heads]: the forward's lse (-inf for a
+ *                     row without visible keys)
+ *   out               the forward's output for the same inputs
+ *   total_q           cu_seqlens_q[batch] (sizes the workspace)
+ *   max_seqlen_q/_k   bound every query / key length (they size the launch)
+ *   workspace         at least rra_varlen_attn_bwd_workspace_bytes(total_q,
+ *                     num_heads) bytes, 16-byte aligned, caller-owned; its
+ *                     contents on entry do not matter
+ * Rows of dq without visible keys are 0; keys no query sees get dk = dv = 0.
+ * Other arguments as for the forward pass.  total_q * num_heads must not
+ * exceed 2^28.  Three kernels run on `stream` (dsum and lse rescale, dq,
+ * dk/dv); the result is deterministic (no atomics).
+ */
+int32_t rra_varlen_attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                            const void *dout, void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float softmax_scale, int32_t causal, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Workspace bytes rra_varlen_attn_bwd needs: 8 * total_q * num_heads (0 if
+ * the sizes are invalid). */
+size_t rra_varlen_attn_bwd_workspace_bytes(int32_t total_q, int32_t num_heads);
+
 /* Query rows per work item of rra_varlen_attn_fwd for this head_dim and
  * max_seqlen_q (0 if head_dim is unsupported or max_seqlen_q < 0).  Work
  * items are (sequence, query tile, head). */

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ("rra_varlen_attn_fwd", "rra_varlen_attn_fwd_gqa", "rra_varlen_attn_fwd_paged", "rra_paged_decode_attn",
+    for n in ("rra_varlen_attn_fwd", "rra_varlen_attn_fwd_gqa", "rra_varlen_attn_fwd_paged", "rra_varlen_attn_bwd",
+              "rra_varlen_attn_bwd_workspace_bytes", "rra_paged_decode_attn",
               "rra_paged_decode_workspace_bytes", "rra_paged_decode_state_init", "rra_paged_decode_step",
               "rra_paged_decode_finalize",
               "rra_status_string", "rra_varlen_block_q"):
@@ -121,6 +122,34 @@ def test_varlen_paged_validation(lib, kw, status):
     if status == 0 and kw.get("BS") == 8:
         kw = dict(kw, maxq=0)  # accepted sizes, but nothing to launch here
     assert paged_fwd_status(lib, **kw) == status
+
+
+def bwd_status(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cuq=FAKE, cuk=FAKE,
+             Tq=100, maxq=50, maxk=60, batch=2, H=8, Hkv=2, D=128, scale=0.1, causal=1, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib.rra_varlen_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                                   a["cuq"], a["cuk"], a["Tq"], a["maxq"], a["maxk"], a["batch"], a["H"], a["Hkv"],
+                                   a["D"], a["scale"], a["causal"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 1), (dict(H=0), 1), (dict(Hkv=3), 1), (dict(Tq=-1), 1), (dict(maxq=-1), 1), (dict(maxk=-1), 1),
+    (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(D=48), 2), (dict(Tq=1 << 26, H=8), 1),
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(dk=None), 1), (dict(cuk=None), 1),
+    (dict(dq=FAKE + 8), 1), (dict(out=FAKE + 2), 1), (dict(lse=FAKE + 1), 1),
+    (dict(ws=None), 3), (dict(wsb=100 * 8 * 8 - 4), 3), (dict(ws=FAKE + 4), 3),
+    (dict(batch=0), 0), (dict(maxq=0, maxk=0, q=None), 0),
+])
+def test_bwd_validation(lib, kw, status):
+    assert bwd_status(lib, **kw) == status
+
+
+def test_bwd_workspace_size(lib):
+    assert rra.rra_varlen_attn_bwd_workspace_bytes(100, 8) == 100 * 8 * 8
+    assert rra.rra_varlen_attn_bwd_workspace_bytes(0, 8) == 0
+    assert rra.rra_varlen_attn_bwd_workspace_bytes(-1, 8) == 0
+    assert rra.rra_varlen_attn_bwd_workspace_bytes(10, 0) == 0
 
 
 def decode_status(lib, **kw):

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     rra_varlen_attn_fwd,
     rra_varlen_attn_fwd_gqa,
     rra_varlen_attn_fwd_paged,
+    rra_varlen_attn_bwd,
+    rra_varlen_attn_bwd_workspace_bytes,
     rra_varlen_block_q,
     rra_paged_decode_attn,
     rra_paged_decode_workspace_bytes,
@@ -22,6 +24,7 @@ from .binding import (  # noqa: F401
     rra_debug_paged_gather,
     varlen_attn_fwd,
     varlen_attn_fwd_paged,
+    varlen_attn_bwd,
     paged_decode_attn,
     decode_state_init,
     paged_decode_step,

@@ -54,6 +54,11 @@ def load_library():
     lib.rra_varlen_attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                               f32, i32, vp]
     lib.rra_varlen_attn_fwd_paged.restype = i32
+    lib.rra_varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        f32, i32, vp, sz, vp]
+    lib.rra_varlen_attn_bwd.restype = i32
+    lib.rra_varlen_attn_bwd_workspace_bytes.argtypes = [i32, i32]
+    lib.rra_varlen_attn_bwd_workspace_bytes.restype = sz
     lib.rra_varlen_block_q.argtypes = [i32, i32]
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
@@ -131,6 +136,21 @@ def rra_varlen_attn_fwd_paged(q, k_pool, v_pool, out, lse, cu_seqlens_q, seqlens
         _ptr(block_table), int(max_seqlen_q), int(batch), int(num_heads), int(num_kv_heads), int(head_dim),
         int(block_size), int(max_blocks_per_seq), float(softmax_scale), int(bool(causal)), _stream(stream))
     _check("rra_varlen_attn_fwd_paged", st)
+
+
+def rra_varlen_attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, total_q, max_seqlen_q,
+                        max_seqlen_k, batch, num_heads, num_kv_heads, head_dim, softmax_scale, causal, workspace,
+                        workspace_bytes, stream=None):
+    st = load_library().rra_varlen_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(total_q), int(max_seqlen_q), int(max_seqlen_k), int(batch),
+        int(num_heads), int(num_kv_heads), int(head_dim), float(softmax_scale), int(bool(causal)), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+    _check("rra_varlen_attn_bwd", st)
+
+
+def rra_varlen_attn_bwd_workspace_bytes(total_q, num_heads) -> int:
+    return int(load_library().rra_varlen_attn_bwd_workspace_bytes(int(total_q), int(num_heads)))
 
 
 def rra_paged_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
@@ -217,6 +237,30 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_s
     rra_varlen_attn_fwd_gqa(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, cu_seqlens_q.numel() - 1,
                             H, k.shape[1], D, softmax_scale, causal, stream)
     return out, lse
+
+
+def varlen_attn_bwd(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
+                    causal, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the packed forward pass for the upstream
+    gradient dout; q/out/dout [Tq,H,D], k/v [Tk,Hkv,D] bf16, lse [Tq,H] fp32
+    (the forward's out and lse), cu_seqlens int32 (all device tensors)."""
+    import torch
+    for t in (q, k, v, out, dout):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v, out, dout must be contiguous bfloat16 device tensors")
+    if q.shape != out.shape or q.shape != dout.shape or k.shape != v.shape or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("bad shapes for the backward pass")
+    Tq, H, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = rra_varlen_attn_bwd_workspace_bytes(Tq, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rra_varlen_attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, Tq, max_seqlen_q,
+                        max_seqlen_k, cu_seqlens_q.numel() - 1, H, k.shape[1], D, softmax_scale, causal, workspace,
+                        workspace.numel() * workspace.element_size(), stream)
+    return dq, dk, dv
 
 
 def varlen_attn_fwd_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q, softmax_scale,

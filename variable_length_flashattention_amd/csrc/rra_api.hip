@@ -158,6 +158,64 @@ int32_t rra_varlen_attn_fwd(const void *q, const void *k, const void *v, void *o
                                    num_heads, head_dim, softmax_scale, causal, stream);
 }
 
+size_t rra_varlen_attn_bwd_workspace_bytes(int32_t total_q, int32_t num_heads)
+{
+    if (total_q < 0 || num_heads <= 0) return 0;
+    return 2 * (size_t)total_q * (size_t)num_heads * sizeof(float);
+}
+
+int32_t rra_varlen_attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                            const void *dout, void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float softmax_scale, int32_t causal, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+        return RRA_ERR_INVALID_ARG;
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return RRA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return RRA_ERR_INVALID_ARG;
+    if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
+    // workspace byte offsets are 32-bit inside the kernels
+    if ((int64_t)total_q * num_heads > ((int64_t)1 << 28)) return RRA_ERR_INVALID_ARG;
+    if (batch == 0 || (max_seqlen_q == 0 && max_seqlen_k == 0)) return RRA_OK;
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+        return RRA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return RRA_ERR_INVALID_ARG;
+    const size_t need = rra_varlen_attn_bwd_workspace_bytes(total_q, num_heads);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return RRA_ERR_WORKSPACE;
+
+    BwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.out = static_cast<const uint16_t *>(out);
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.lse = lse;
+    a.dq = static_cast<uint16_t *>(dq);
+    a.dk = static_cast<uint16_t *>(dk);
+    a.dv = static_cast<uint16_t *>(dv);
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.ws = static_cast<float *>(workspace);
+    a.batch = batch;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.gqa_ratio = num_heads / num_kv_heads;
+    a.head_dim = head_dim;
+    a.total_q = total_q;
+    a.levels_q = (int32_t)(((int64_t)max_seqlen_q + kBwdQRows - 1) / kBwdQRows);
+    a.levels_k = (int32_t)(((int64_t)max_seqlen_k + kBwdKRows - 1) / kBwdKRows);
+    a.n_items_q = (int64_t)batch * a.levels_q * num_heads;
+    a.n_items_k = (int64_t)batch * a.levels_k * num_kv_heads;
+    a.scale = softmax_scale;
+    a.scale_log2 = softmax_scale * kLog2e;
+    return hip_status(launch_varlen_bwd(a, causal == 1, device_cus(), static_cast<hipStream_t>(stream)));
+}
+
 int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,
                                   int32_t max_seqlen_q, int32_t head_dim, int32_t *items_out, int64_t capacity,
                                   int64_t *item_count, void *stream)

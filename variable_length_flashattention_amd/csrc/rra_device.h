@@ -56,6 +56,13 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void *
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
+// 4 bytes per lane from buffer `r` at byte offset voff + soff straight into
+// LDS: lane l writes lds + 4*l (lds is wave-uniform).
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, int32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
+}
+
 // max of three floats in one instruction.  Operands are finite or -inf here,
 // so the NaN canonicalisation the compiler would add around fmaxf is not needed.
 __device__ __forceinline__ float max3f(float a, float b, float c)

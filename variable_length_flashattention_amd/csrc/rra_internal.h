@@ -40,6 +40,26 @@ struct VarlenArgs {
     int32_t bs_shift, max_blocks;
 };
 
+// Backward pass of the packed forward pass.  Workspace: lse2 and dsum,
+// fp32 [num_heads][total_q] each (head-major, so a head's consecutive query
+// rows are contiguous): lse2 = lse * log2(e) (+inf where lse = -inf), dsum =
+// rowsum(dout * out).
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *out, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    const int32_t *cu_q, *cu_k;
+    float *ws;           // lse2 [H][total_q] then dsum [H][total_q]
+    int32_t batch, num_heads, num_kv_heads, gqa_ratio, head_dim;
+    int32_t total_q;
+    int32_t levels_q, levels_k;   // ceil(max_seqlen / tile) for the two work lists
+    int64_t n_items_q, n_items_k; // batch * levels * heads (dq items over q heads, dk/dv items over kv heads)
+    float scale, scale_log2;
+};
+constexpr int kBwdQRows = 128;  // query rows per dq work item
+constexpr int kBwdKRows = 128;  // keys per dk/dv work item
+hipError_t launch_varlen_bwd(const BwdArgs &a, bool causal, int num_cus, hipStream_t stream);
+
 hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream);
 hipError_t launch_varlen_tile_map(const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
                                   int32_t block_q, int32_t levels, int64_t n_items, int32_t *items_out,
