@@ -370,7 +370,7 @@ def main():
                          "TFLOP/s": round(2.5 * flops / b_avg / 1e12, 2),
                          "frac_mfma_peak": round(2.5 * flops / b_avg / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "avg_call_us": round(b_avg * 1e6, 2),
-                         "note": "prep + dq + dk/dv kernels per call; flops = 2.5 x forward (S, dP, dV, dK, dQ)"}
+                         "note": "dq (+ dsum) and dk/dv kernels per call; flops = 2.5 x forward (S, dP, dV, dK, dQ)"}
     del brun
     torch.cuda.empty_cache()
 

@@ -139,8 +139,9 @@ int32_t rra_varlen_attn_fwd_paged(const void *q, const void *k_pool, const void 
  *                     contents on entry do not matter
  * Rows of dq without visible keys are 0; keys no query sees get dk = dv = 0.
  * Other arguments as for the forward pass.  total_q * num_heads must not
- * exceed 2^28.  Three kernels run on `stream` (dsum and lse rescale, dq,
- * dk/dv); the result is deterministic (no atomics).
+ * exceed 2^28.  Two kernels run on `stream` (dq, which also leaves the
+ * rows' dout.out and rescaled lse in the workspace, then dk/dv); the result
+ * is deterministic (no atomics).
  */
 int32_t rra_varlen_attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
                             const void *dout, void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q,

@@ -10,14 +10,15 @@
 // (dsum_i equals sum_j P_ij dP_ij, the softmax Jacobian's row term).
 // Grouped-query K/V: the dK and dV of kv head kh sum over its query heads.
 //
-// Three kernels, no atomics, deterministic:
-//   1. varlen_bwd_prep_kernel: dsum and lse * log2(e), head-major.
-//   2. varlen_bwd_dq_kernel: one work item per (sequence, 128-query tile,
+// Two kernels, no atomics, deterministic:
+//   1. varlen_bwd_dq_kernel: one work item per (sequence, 128-query tile,
 //      head), the forward's work list; each wave owns 32 query rows (Q and
-//      dO in VGPRs) and walks the key tiles, staged into LDS:
+//      dO in VGPRs), forms dsum of its rows from dO and out, and walks the
+//      key tiles, staged into LDS:
 //        S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
-//      (the S^T orientation of the forward: a query per lane column).
-//   3. varlen_bwd_dkv_kernel: one work item per (sequence, 128-key block,
+//      (the S^T orientation of the forward: a query per lane column).  It
+//      also stores dsum and lse * log2(e) head-major for the next kernel.
+//   2. varlen_bwd_dkv_kernel: one work item per (sequence, 128-key block,
 //      kv head); each wave owns 32 keys (K and V in VGPRs) and walks the
 //      32-row query tiles of every query head of the group, staged into LDS:
 //        S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
@@ -116,39 +117,8 @@ __device__ __forceinline__ void store_rows_T(uint16_t *row_ptr, const f32x16 (&a
 }
 
 // ---------------------------------------------------------------------------
-// 1. dsum = rowsum(dout * out) and lse2 = lse * log2(e), head-major.
-template <int D>
-__global__ __launch_bounds__(256) void varlen_bwd_prep_kernel(BwdArgs a)
-{
-    constexpr int LP = D / 8;          // lanes per row (8 bf16 each)
-    constexpr int RPW = 64 / LP;       // rows per wave
-    const int lane = threadIdx.x & 63;
-    const int64_t rows = (int64_t)a.total_q * a.num_heads;
-    const int64_t first = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LP;
-    const int64_t step = (int64_t)gridDim.x * 4 * RPW;
-    for (int64_t row = first; row - lane / LP < rows; row += step) {
-        float acc = 0.f;
-        if (row < rows) {
-            const u32x4 o = load16(a.out + row * D + 8 * (lane % LP));
-            const u32x4 g = load16(a.dout + row * D + 8 * (lane % LP));
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                acc += bf16lo_to_f32(o[e]) * bf16lo_to_f32(g[e]) + bf16hi_to_f32(o[e]) * bf16hi_to_f32(g[e]);
-        }
-#pragma unroll
-        for (int off = 1; off < LP; off <<= 1) acc += __shfl_xor(acc, off, 64);
-        if (row < rows && lane % LP == 0) {
-            const int t = (int)(row / a.num_heads), h = (int)(row % a.num_heads);
-            const float l = a.lse[row];
-            const int64_t idx = (int64_t)h * a.total_q + t;
-            a.ws[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
-            a.ws[(int64_t)a.num_heads * a.total_q + idx] = acc;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dQ.  Same work list and query layout as the forward kernel.
+// 1. dQ (and dsum, lse2).  Same work list and query layout as the forward
+// kernel.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void varlen_bwd_dq_kernel(BwdArgs a)
 {
@@ -165,7 +135,7 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void varlen_bwd_dq_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.num_heads, Hkv = a.num_kv_heads;
     const float sl2 = a.scale_log2;
-    const float *ws_lse2 = a.ws, *ws_dsum = a.ws + (int64_t)H * a.total_q;
+    float *ws_lse2 = a.ws, *ws_dsum = a.ws + (int64_t)H * a.total_q;
     const WorkTables wt = build_work_tables(a.cu_q, a.cu_k, a.batch + 1, a.batch, BQ, a.levels_q, sched, kSchedInts);
 
     for (int64_t k = 0;; k++) {
@@ -215,8 +185,29 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void varlen_bwd_dq_kernel(
                 gf[ks] = as_bf16x8(load16(a.dout + off + 16 * ks));
             }
         }
-        const float lse2 = ws_lse2[(int64_t)h * a.total_q + q0 + qr];
-        const float dsum = ws_dsum[(int64_t)h * a.total_q + q0 + qr];
+        // dsum = dO . out of the row (each half-wave holds half of d), and
+        // lse2 = lse * log2(e) (+inf for a row without visible keys, so that
+        // every probability of the row is 0); stored for the dk/dv kernel
+        float dsum, lse2;
+        {
+            const int64_t row = (int64_t)(q0 + qr) * H + h;
+            const uint16_t *orow = a.out + row * D + 8 * (lane >> 5);
+            float part = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) {
+                const u32x4 o4 = load16(orow + 16 * ks), g4 = __builtin_bit_cast(u32x4, gf[ks]);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    part += bf16lo_to_f32(o4[e]) * bf16lo_to_f32(g4[e]) + bf16hi_to_f32(o4[e]) * bf16hi_to_f32(g4[e]);
+            }
+            dsum = sum_across_halves(part);
+            const float l = a.lse[row];
+            lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+            if (row_ok && lane < 32) {
+                ws_lse2[(int64_t)h * a.total_q + q0 + my_i] = lse2;
+                ws_dsum[(int64_t)h * a.total_q + q0 + my_i] = dsum;
+            }
+        }
         f32x16 acc[NDC];
 #pragma unroll
         for (int dc = 0; dc < NDC; dc++)
@@ -288,7 +279,7 @@ template <int D>
 constexpr int bwd_dkv_split() { return D == 256 ? 2 : 1; }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void varlen_bwd_dkv_kernel(BwdArgs a)
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void varlen_bwd_dkv_kernel(BwdArgs a)
 {
     using T = BwdTile<D>;
     constexpr int NW = T::NW, BKB = kBwdKRows, BQB = 32, TB = BQB * T::ROWB;
@@ -377,14 +368,29 @@ __global__ __launch_bounds__(256, 1) void varlen_bwd_dkv_kernel(BwdArgs a)
             // some pair of this wave's keys and the tile's rows visible?
             const int qlast = min(qbase + BQB - 1, Lq - 1);
             if (kw0 >= Lk || (CAUSAL && kw0 > qlast + diag)) return;
-            // S = Q K^T, dP = dO V^T (rows = queries, cols = keys)
+            // S = Q K^T, then dP = dO V^T (rows = queries, cols = keys); the
+            // row operands are read RA MMAs ahead, and the scheduling
+            // barriers keep the two chains apart (interleaved, they keep
+            // both accumulators and all their operands live at once)
             f32x16 s, dp;
 #pragma unroll
             for (int r = 0; r < 16; r++) s[r] = dp[r] = 0.f;
+            {
+                constexpr int NM = 2 * NKS, RA = 2;
+                auto rd = [&](int m) __attribute__((always_inline)) -> bf16x8 {
+                    return read_rows<D>(m < NKS ? Qb : Gb, 0, m % NKS, lane);
+                };
+                bf16x8 op[RA];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ks++) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(Qb, 0, ks, lane), kf[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(Gb, 0, ks, lane), vf[ks], dp, 0, 0, 0);
+                for (int m = 0; m < RA; m++) op[m] = rd(m);
+#pragma unroll
+                for (int m = 0; m < NM; m++) {
+                    const bf16x8 x = op[m % RA];
+                    if (m + RA < NM) op[m % RA] = rd(m + RA);
+                    if (m < NKS) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, kf[m], s, 0, 0, 0);
+                    else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, vf[m - NKS], dp, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             const bool need_mask = (qbase + BQB > Lq) || (kw0 + 32 > Lk) || (CAUSAL && kw0 + 31 > qbase + diag);
             uint32_t pp[8], pd[8];
@@ -409,13 +415,25 @@ __global__ __launch_bounds__(256, 1) void varlen_bwd_dkv_kernel(BwdArgs a)
                 pd[2 * j + 1] = pack_bf16x2(dv4[2], dv4[3]);
             }
             // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per MMA
+            {
+                // MMA n: m = n / (2 NDC), dc = n / 2 % NDC, dV (even n) or dK (odd n)
+                constexpr int NM = 4 * NDC, RA = 2;
+                auto rd = [&](int n) __attribute__((always_inline)) -> bf16x8 {
+                    return read_cols<D>(n & 1 ? Qb : Gb, n / (2 * NDC), dc0 + n / 2 % NDC, lane);
+                };
+                bf16x8 op[RA];
 #pragma unroll
-            for (int m = 0; m < 2; m++)
+                for (int n = 0; n < RA; n++) op[n] = rd(n);
 #pragma unroll
-                for (int dc = 0; dc < NDC; dc++) {
-                    dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols<D>(Gb, m, dc0 + dc, lane), packed_b(pp, m), dv[dc], 0, 0, 0);
-                    dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols<D>(Qb, m, dc0 + dc, lane), packed_b(pd, m), dk[dc], 0, 0, 0);
+                for (int n = 0; n < NM; n++) {
+                    const bf16x8 x = op[n % RA];
+                    if (n + RA < NM) op[n % RA] = rd(n + RA);
+                    const int m = n / (2 * NDC), dc = n / 2 % NDC;
+                    if (n & 1) dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, packed_b(pd, m), dk[dc], 0, 0, 0);
+                    else dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, packed_b(pp, m), dv[dc], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            }
         };
         for (int t = 0; t < ntiles; t += 2) {
             tile(t, q_lds0, g_lds0, st_lds0, q_lds1, g_lds1, st_lds1);
@@ -432,17 +450,9 @@ __global__ __launch_bounds__(256, 1) void varlen_bwd_dkv_kernel(BwdArgs a)
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs &a, bool causal, int num_cus, hipStream_t stream)
 {
-    {
-        const int64_t rows = (int64_t)a.total_q * a.num_heads;
-        const int64_t per_block = 4 * (64 / (D / 8));
-        int64_t blocks = (rows + per_block - 1) / per_block;
-        if (blocks > (int64_t)num_cus * 16) blocks = (int64_t)num_cus * 16;
-        if (blocks > 0)
-            hipLaunchKernelGGL((varlen_bwd_prep_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    }
     BwdArgs ak = a;
     ak.n_items_k *= bwd_dkv_split<D>();  // items per (block, kv head) d range
-    const int64_t slots_q = (int64_t)num_cus * (D == 256 ? 1 : 2), slots_k = num_cus;
+    const int64_t slots_q = (int64_t)num_cus * (D == 256 ? 1 : 2), slots_k = (int64_t)num_cus * (D == 64 ? 2 : 1);
     const dim3 gq((unsigned)(a.n_items_q < slots_q ? a.n_items_q : slots_q));
     const dim3 gk((unsigned)(ak.n_items_k < slots_k ? ak.n_items_k : slots_k));
     if (a.n_items_q > 0) {
