@@ -293,7 +293,11 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             // K fragments are read KD MMAs ahead of use; the scheduling
             // barriers keep the compiler from sinking the reads next to
             // their MMAs (it does that under register pressure, and each
-            // MMA then waits out a full LDS latency)
+            // MMA then waits out a full LDS latency).  The wave runs this
+            // phase at raised priority, so that a SIMD shared with a wave in
+            // its softmax keeps issuing these MMAs first (measured: ~3 %
+            // faster on the mixed workload, ~2 % slower on the skewed one).
+            __builtin_amdgcn_s_setprio(1);
             {
                 constexpr int NM = NC * NKS, KD = 3;
                 auto kread = [&](int m) -> bf16x8 {
@@ -316,6 +320,7 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             uint32_t pk[RPW][NC][8];
 #pragma unroll
             for (int u = 0; u < RPW; u++) {
