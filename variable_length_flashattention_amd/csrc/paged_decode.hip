@@ -388,12 +388,32 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     const int w_first = min(gs0 / P, a.n_ranges - 1);
     const int npieces = gs1 > gs0 ? min((gs1 - 1) / P, a.n_ranges - 1) - w_first + 1 : 0;
     auto slot = [&](int c) -> int64_t { return (int64_t)(w_first + c + s) * a.num_q_heads + qh; };
-    float M = -INFINITY;
-    for (int c = lane; c < npieces; c += 64) M = fmaxf(M, a.ws_m[slot(c)]);
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    // stateful step: the caller's state is one more piece (m in scaled units)
+    const int sub = lane / LP, dl = lane % LP;  // this lane's piece within a load, and d chunk
+    // One round trip for the common case: m and l of pieces 0..63 (one per
+    // lane), this wave's first KPRE o loads, and the caller's state max.
+    // Loads past the last piece read the last piece (weight 0).
+    constexpr int KPRE = 2;
     const bool stateful = a.st_m != nullptr;
     const float m_prev = stateful ? a.st_m[pair] : -INFINITY;
+    float m_c = -INFINITY, l_c = 0.f;
+    if (lane < npieces) {
+        m_c = a.ws_m[slot(lane)];
+        l_c = a.ws_l[slot(lane)];
+    }
+    f32x4 opre[KPRE][NA];
+    if (npieces > 0) {
+#pragma unroll
+        for (int k = 0; k < KPRE; k++) {
+            const int cc = min(wave * PPL + k * NWC * PPL + sub, npieces - 1);
+            const float *oc = a.ws_o + slot(cc) * D + 4 * dl;
+#pragma unroll
+            for (int i = 0; i < NA; i++) opre[k][i] = *reinterpret_cast<const f32x4 *>(oc + 4 * LP * i);
+        }
+    }
+    float M = m_c;
+    for (int c = 64 + lane; c < npieces; c += 64) M = fmaxf(M, a.ws_m[slot(c)]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    // stateful step: the caller's state is one more piece (m in scaled units)
     const float M_s = fmaxf(m_prev, M == -INFINITY ? -INFINITY : M * a.scale);  // merged max, scaled units
     if (stateful && M_s == -INFINITY) return;  // nothing seen yet and nothing new (uniform in the workgroup)
     const float m_use = stateful ? M_s / a.scale : (M == -INFINITY ? 0.f : M);
@@ -401,19 +421,30 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     f32x4 acc[NA];
 #pragma unroll
     for (int i = 0; i < NA; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int sub = lane / LP, dl = lane % LP;  // this lane's piece within a load, and d chunk
     for (int c0 = 0; c0 < npieces; c0 += 64) {
         // lane j holds piece c0 + j: its weight 2^{(m_c - M) c} (0 past the end)
         const int c = c0 + lane;
         float wgt = 0.f;
         if (c < npieces) {
-            wgt = fast_exp2((a.ws_m[slot(c)] - m_use) * a.scale_log2);
-            L += a.ws_l[slot(c)] * wgt;
+            const float mc = c0 == 0 ? m_c : a.ws_m[slot(c)];
+            wgt = fast_exp2((mc - m_use) * a.scale_log2);
+            L += (c0 == 0 ? l_c : a.ws_l[slot(c)]) * wgt;
         }
         const int n = min(64, npieces - c0);
-        // this wave's loads: pieces wave*PPL + k*NWC*PPL (+ sub) of the chunk
+        // this wave's loads: pieces wave*PPL + k*NWC*PPL (+ sub) of the chunk;
+        // in the first chunk the first KPRE of them are already in registers
+        int j = wave * PPL;
+        if (c0 == 0) {
+#pragma unroll
+            for (int k = 0; k < KPRE; k++, j += NWC * PPL) {
+                const int jj = j + sub;
+                const float wj = __shfl(wgt, jj & 63, 64);
+#pragma unroll
+                for (int i = 0; i < NA; i++) acc[i] += (jj < n ? wj : 0.f) * opre[k][i];
+            }
+        }
 #pragma unroll 4
-        for (int j = wave * PPL; j < n; j += NWC * PPL) {
+        for (; j < n; j += NWC * PPL) {
             const int jj = j + sub;  // this lane's piece, relative to c0
             const float wj = __shfl(wgt, jj & 63, 64);
             const int cc = min(c0 + jj, npieces - 1);  // (weight 0 past the end)
