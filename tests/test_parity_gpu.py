@@ -30,6 +30,9 @@ EDGE_CASES = [
     ("d256", [1, 33, 160, 64], [1, 33, 170, 64], 2, 256),
     ("d64_many", list(range(1, 40)), list(range(1, 40)), 1, 64),
     ("single_long", [700], [700], 1, 128),
+    # more sequences than the LDS work tables hold: items decode from global memory
+    ("many_seqs_global", np.random.Generator(np.random.PCG64(61)).integers(0, 9, 2000).tolist(),
+     np.random.Generator(np.random.PCG64(62)).integers(0, 9, 2000).tolist(), 2, 64),
 ]
 
 
