@@ -49,6 +49,7 @@ def parse():
 
 VARLEN_SOURCES = ("varlen_fwd.hip", "tile_map.h", "rra_device.h", "rra_internal.h", "rra_api.hip")
 DECODE_SOURCES = ("paged_decode.hip", "rra_device.h", "rra_internal.h", "rra_api.hip")
+BWD_SOURCES = ("varlen_bwd.hip", "tile_map.h", "rra_device.h", "rra_internal.h", "rra_api.hip")
 
 
 def kernel_source_hash(files=None):
@@ -66,25 +67,25 @@ def dev_bf16(torch, bits):
 
 
 def time_launches(torch, fn, steps, warmup):
-    """Warm up, then time exactly `steps` launches: wall time bracketed by
-    synchronize, plus per-launch HIP event pairs on the current stream."""
+    """Warm up, then time exactly `steps` back-to-back launches: wall time
+    bracketed by synchronize, and one HIP event pair around the whole timed
+    region on the current stream (the stream the library launches on).
+    Returns (wall seconds, event seconds per launch)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     if torch.distributed.is_available() and torch.distributed.is_initialized():
         torch.distributed.barrier()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         fn()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3  # seconds
-    return wall, per
+    return wall, start.elapsed_time(end) * 1e-3 / steps
 
 
 class VarlenRun:
@@ -218,7 +219,7 @@ class DecodeStepsRun:
         r.rra_paged_decode_finalize(self.l, self.o, self.out, S, Hq, D)
 
 
-def cpu_baseline(case, n_rows=131072, seed=7):
+def cpu_baseline(case, n_rows=655360, seed=7):
     """The fp64 oracle, as it stands, on a bounded random sample of the same
     workload's (token, head) rows; reported in the metric's unit."""
     import oracle as O
@@ -290,21 +291,20 @@ def main():
         else:
             r = VarlenRun(torch, case)
             nbytes, flops = I.varlen_bytes(case), I.varlen_flops(case)
-        _, p = time_launches(torch, r, args.steps, args.warmup)
-        t = float(np.mean(p))
+        _, t = time_launches(torch, r, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "avg_us": round(t * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 2),
                           "GB/s": round(nbytes / t / 1e9, 1), "kernel_source_hash": src_hash,
                           "varlen_source_hash": kernel_source_hash(VARLEN_SOURCES),
-                          "decode_source_hash": kernel_source_hash(DECODE_SOURCES)}), flush=True)
+                          "decode_source_hash": kernel_source_hash(DECODE_SOURCES),
+                          "bwd_source_hash": kernel_source_hash(BWD_SOURCES)}), flush=True)
         return
 
     mixed = I.mixed()
     flops = I.varlen_flops(mixed)
     run = VarlenRun(torch, mixed)
-    wall, per = time_launches(torch, run, args.steps, args.warmup)
+    wall, avg_launch = time_launches(torch, run, args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
     value = flops / (wall / args.steps) / 1e12
-    avg_launch = float(np.mean(per))
     achieved = flops / avg_launch / 1e12
     lines = {
         "metric": "varlen attn fwd TFLOP/s + % bf16 MFMA peak; paged decode HBM GB/s",
@@ -327,7 +327,6 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic("varlen_fwd_mixed", kernel_source_hash(VARLEN_SOURCES)),
                      "kernel": "varlen_fwd_kernel<128,true>", "avg_launch_us": round(avg_launch * 1e6, 2),
-                     "median_launch_us": round(float(np.median(per)) * 1e6, 2),
                      "algorithmic_bytes": I.varlen_bytes(mixed)},
     }
 
@@ -340,9 +339,8 @@ def main():
     # paged decode (second row of the metric)
     dec = I.paged_decode()
     drun = DecodeRun(torch, dec)
-    dwall, dper = time_launches(torch, drun, args.steps, args.warmup)
+    _, d_avg = time_launches(torch, drun, args.steps, args.warmup)
     dbytes = I.decode_bytes(dec)
-    d_avg = float(np.mean(dper))
     lines["decode"] = {"workload": "paged GQA decode: 64 seqs, ctx U[1,8192] (seed 5001), Hq=32, Hkv=8, "
                                    "head_dim 128, 16-token blocks, permuted block table",
                        "GB/s": round(dbytes / d_avg / 1e9, 1), "frac_of_hbm_peak": round(dbytes / d_avg / 1e9 / PEAK_HBM_GBS, 4),
@@ -352,8 +350,7 @@ def main():
                        "note": "offsets + range + combine kernels per call; working set exceeds the 256 MiB MALL"}
     del drun
     srun = DecodeStepsRun(torch, dec)
-    _, sper = time_launches(torch, srun, args.steps, args.warmup)
-    s_avg = float(np.mean(sper))
+    _, s_avg = time_launches(torch, srun, args.steps, args.warmup)
     lines["decode"]["stateful_4_steps"] = {
         "GB/s": round(dbytes / s_avg / 1e9, 1), "frac_of_hbm_peak": round(dbytes / s_avg / 1e9 / PEAK_HBM_GBS, 4),
         "avg_us": round(s_avg * 1e6, 2),
@@ -364,12 +361,12 @@ def main():
     # backward of the mixed workload (5 matmuls' worth of algorithmic flops:
     # 2.5x the forward's)
     brun = BwdRun(torch, mixed)
-    _, bper = time_launches(torch, brun, args.steps, args.warmup)
-    b_avg = float(np.mean(bper))
+    _, b_avg = time_launches(torch, brun, args.steps, args.warmup)
     lines["backward"] = {"workload": "backward of the mixed workload (dq, dk, dv from out, lse, dout)",
                          "TFLOP/s": round(2.5 * flops / b_avg / 1e12, 2),
                          "frac_mfma_peak": round(2.5 * flops / b_avg / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "avg_call_us": round(b_avg * 1e6, 2),
+                         "traffic": load_traffic("varlen_bwd_mixed", kernel_source_hash(BWD_SOURCES)),
                          "note": "dq (+ dsum) and dk/dv kernels per call; flops = 2.5 x forward (S, dP, dV, dK, dQ)"}
     del brun
     torch.cuda.empty_cache()
@@ -388,8 +385,7 @@ def main():
             ("many_short_d256_noncausal", I.many_short(256, False), "hbm"),
         ]:
             r = PagedRun(torch, case) if isinstance(case, I.PagedPrefillCase) else VarlenRun(torch, case)
-            _, p = time_launches(torch, r, 20, 3)
-            t = float(np.mean(p))
+            _, t = time_launches(torch, r, 20, 3)
             dense = case.dense if isinstance(case, I.PagedPrefillCase) else case
             f, b = I.varlen_flops(dense), I.varlen_bytes(dense)
             ctx[name] = {"avg_us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 2),
