@@ -66,11 +66,23 @@ def dev_bf16(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def time_launches(torch, fn, steps, warmup):
-    """Warm up, then time exactly `steps` back-to-back launches: wall time
-    bracketed by synchronize, and one HIP event pair around the whole timed
-    region on the current stream (the stream the library launches on).
+SETTLE_S = 0.5  # seconds of untimed back-to-back launches before the warm-up steps
+
+
+def time_launches(torch, fn, steps, warmup, settle_s=SETTLE_S):
+    """Settle, warm up, then time exactly `steps` back-to-back launches: wall
+    time bracketed by synchronize, and one HIP event pair around the whole
+    timed region on the current stream (the stream the library launches on).
+    The settle phase runs the same launches untimed for `settle_s` seconds:
+    the GPU's clocks ramp up over the first ~0.1 s of sustained work (the
+    mixed forward runs ~25 % slower in its first 50 launches than after 200),
+    and the figure wanted is the sustained rate.
     Returns (wall seconds, event seconds per launch)."""
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
