@@ -371,10 +371,10 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
 
             // O^T += V^T P^T, 16 keys per MMA; each V operand read feeds every
             // active row block
-            // V^T fragments (two transposed reads each) one MMA ahead of use
+            // V^T fragments (two transposed reads each) read VD MMAs ahead of use
             const int g = lane >> 4, j = lane & 15;
             {
-                constexpr int NM = (BK / 16) * NDC, VD = 2;
+                constexpr int NM = (BK / 16) * NDC, VD = 3;
                 auto vread = [&](int mm) -> u32x4 {
                     const int m = mm / NDC, dc = mm % NDC;
                     const int row = 16 * m + 4 * (g >> 1) + (j >> 2);
