@@ -359,7 +359,7 @@ def main():
                        "avg_call_us": round(d_avg * 1e6, 2), "bytes_per_call": dbytes,
                        "traffic": load_traffic("paged_decode", kernel_source_hash(DECODE_SOURCES)),
                        "context_tokens": int(dec.context_lens.sum()),
-                       "note": "offsets + range + combine kernels per call; working set exceeds the 256 MiB MALL"}
+                       "note": "range-split + combine kernels per call (an offsets kernel too above 256 sequences); working set exceeds the 256 MiB MALL"}
     del drun
     srun = DecodeStepsRun(torch, dec)
     _, s_avg = time_launches(torch, srun, args.steps, args.warmup)

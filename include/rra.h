@@ -182,9 +182,10 @@ int32_t rra_varlen_block_q(int32_t head_dim, int32_t max_seqlen_q);
  * out = sum_t softmax_t(softmax_scale * q . K_t) V_t over t < context_lens[s],
  * and out = 0 for a sequence with context length 0.  Context lengths
  * outside [0, max_blocks_per_seq*block_size] are clamped into it, and the sum
- * over sequences of ceil(ctx / 16) must stay below 2^31.  Three kernels run
- * on `stream`: the token-group offsets of the sequences, the partial states
- * of equal ranges of token groups, then a combine that writes out.
+ * over sequences of ceil(ctx / 16) must stay below 2^31.  Two kernels run on
+ * `stream`: the partial states of equal ranges of token groups, then a
+ * combine that writes out; above 256 sequences a first kernel writes the
+ * sequences' token-group offsets into the workspace.
  */
 int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *block_table, const int32_t *context_lens, void *out,
