@@ -12,7 +12,7 @@
 // One workgroup of NW waves owns a work item (sequence b, query tile qt,
 // head h) of BQ = 32*NW query rows; each wave owns a 32-row block of the tile.
 // Key tiles of BK keys are staged global->LDS with direct-to-LDS loads,
-// NBUF-deep so that loads run ahead of the compute.  Per key tile each wave
+// double-buffered so that loads run ahead of the compute.  Per key tile each wave
 //   S^T[key][query] = K . Q^T          (v_mfma_f32_32x32x16_bf16, Q in VGPRs)
 //   masks the tail and the causal diagonal (bottom-right: j <= i + Lk - Lq),
 //   updates m and l (exp2 with log2(e) folded into the scale; l sums the fp32
@@ -41,7 +41,7 @@ struct VarlenTile {
     static constexpr int NW = 4;                       // waves per workgroup
     static constexpr int BQ = 32 * NW * RPW;           // query rows per work item
     static constexpr int BK = D <= 128 ? 64 : 32;
-    static constexpr int NBUF = 2;                     // K/V tiles in flight + in use
+    static constexpr int NBUF = 2;                     // K/V tile buffers (one in flight, one in use)
     static constexpr int ROWB = D * 2;                 // bytes per K/V row
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
     static constexpr int TILE_BYTES = BK * ROWB;       // one K (or V) tile
@@ -66,23 +66,16 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
     constexpr int NC = BK / 32;          // 32-key accumulator tiles per key tile
     constexpr int NKS = D / 16;          // k-steps of the QK^T MMA
     constexpr int NDC = D / 32;          // 32-wide d chunks of the output
-    constexpr int NBUF = T::NBUF;
-    constexpr int LOADS = 2 * T::WAVE_LOADS;  // direct-to-LDS loads per lane per key tile
-    static_assert(NBUF >= 2 && NBUF <= 4, "buffer count");
-    // (paged: the table fetch issued with a tile's loads is covered by the
-    // full wait at the top of the next tile only when NBUF == 2)
-    static_assert(!PAGED || NBUF == 2, "paged staging assumes two buffers");
-    // K and V tiles, NBUF buffers each, as distinct LDS objects: the compiler
+    // Two K/V buffers: each tile waits for every load issued before it (its
+    // own tile, and in paged mode the table fetch for the next) at its top.
+    static_assert(T::NBUF == 2, "the staging assumes two buffers");
+    // K and V tiles, two buffers each, as distinct LDS objects: the compiler
     // then knows a read of one buffer does not depend on direct-to-LDS loads
     // still in flight into another, and does not wait for them.
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TB];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TB];
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[NBUF > 2 ? TB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[NBUF > 2 ? TB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds3[NBUF > 3 ? TB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds3[NBUF > 3 ? TB : 16];
 
     __shared__ int sched[kSchedInts];
 
@@ -229,8 +222,6 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             else stage_packed(kt, kb, vb);
         };
         if (nkt > 0) stage(0, k_lds0, v_lds0);
-        if (NBUF > 2 && nkt > 1) stage(1, k_lds1, v_lds1);
-        if (NBUF > 3 && nkt > 2) stage(2, k_lds2, v_lds2);
 
         // Q^T operand: lane holds Q[my_i][16*ks + 8*(lane/32) .. +7]
         // (rows past the sequence end read its last row; their results are
@@ -261,18 +252,13 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             l_run[u] = 0.f;
         }
 
-        // one key tile; tile kt lives in buffer kt % NBUF, and the tile NBUF-1
-        // ahead is staged into the buffer tile kt-1 used
+        // one key tile; tile kt lives in buffer kt % 2, and tile kt+1 is
+        // staged into the buffer tile kt-1 used
         auto tile = [&](int kt, const uint8_t *Kb, const uint8_t *Vb, uint8_t *kn, uint8_t *vn) {
             const int kbase = kt * BK;
-            // this wave's loads of tile kt are done once at most those of the
-            // later tiles already issued (up to NBUF-2) remain in flight
-            const int later = min(NBUF - 2, nkt - 1 - kt);
-            if (NBUF > 3 && later >= 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-            else if (NBUF > 2 && later >= 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-            else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt are done
             __syncthreads();  // tile kt visible; every wave is done with tile kt-1
-            if (kt + NBUF - 1 < nkt) stage(kt + NBUF - 1, kn, vn);
+            if (kt + 1 < nkt) stage(kt + 1, kn, vn);
             bool act[RPW];
             bool any = false;
 #pragma unroll
@@ -405,24 +391,9 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                 }
             }
         };
-        if constexpr (NBUF == 2) {
-            for (int kt = 0; kt < nkt; kt += 2) {
-                tile(kt, k_lds0, v_lds0, k_lds1, v_lds1);
-                if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-            }
-        } else if constexpr (NBUF == 3) {
-            for (int kt = 0; kt < nkt; kt += 3) {
-                tile(kt, k_lds0, v_lds0, k_lds2, v_lds2);
-                if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-                if (kt + 2 < nkt) tile(kt + 2, k_lds2, v_lds2, k_lds1, v_lds1);
-            }
-        } else {
-            for (int kt = 0; kt < nkt; kt += 4) {
-                tile(kt, k_lds0, v_lds0, k_lds3, v_lds3);
-                if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-                if (kt + 2 < nkt) tile(kt + 2, k_lds2, v_lds2, k_lds1, v_lds1);
-                if (kt + 3 < nkt) tile(kt + 3, k_lds3, v_lds3, k_lds2, v_lds2);
-            }
+        for (int kt = 0; kt < nkt; kt += 2) {
+            tile(kt, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
 
         // epilogue: out = O / l (0 when no key is visible), lse = scale*m + ln l (-inf then)
