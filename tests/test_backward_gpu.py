@@ -74,6 +74,7 @@ CASES = [
     ("gqa_4to1", [150, 260], [150, 260], 8, 2, 128),
     ("d256", [140, 33], [140, 300], 2, 1, 256),
     ("d64_many", list(range(1, 40, 3)), list(range(1, 40, 3)), 4, 2, 64),
+    ("long_d64", [3000, 7], [3000, 700], 2, 1, 64),      # 94 query tiles, 24 key blocks
     # more sequences than the LDS work tables hold (both kernels decode items from global memory)
     ("many_seqs_global", np.random.Generator(np.random.PCG64(63)).integers(0, 7, 2000).tolist(),
      np.random.Generator(np.random.PCG64(64)).integers(0, 7, 2000).tolist(), 2, 1, 64),

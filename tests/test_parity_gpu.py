@@ -106,6 +106,18 @@ def test_full_size_sampled(name, make, causal):
     compare(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, f"{name} causal={causal} rows={len(rows)}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_sequence_sampled(causal):
+    """One 32768-token sequence (256 query tiles, 512 key tiles at head_dim 128)
+    beside a 1-token one: every row written, sampled rows against the oracle."""
+    c = I.varlen_case("long", [32768, 1], [32768, 1], 2, 128, seed=777, causal=causal)
+    out, lse = run_varlen(c)
+    assert np.all(np.isfinite(lse)), "some (token, head) row was not written"
+    rows = sample_rows(c, n_random=128)
+    ro, rl = O.varlen_attn_rows(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, rows)
+    compare(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, f"long causal={causal} rows={len(rows)}")
+
+
 def test_deterministic():
     c = I.mixed()
     a = run_varlen(c)
