@@ -1,4 +1,5 @@
-"""MI355X (gfx950) variable-length FlashAttention forward and paged GQA decode.
+"""MI355X (gfx950) variable-length FlashAttention: forward (packed or paged
+K/V, grouped-query), backward, and paged GQA decode (one-shot or stateful).
 
 The compute lives in ``librra.so`` (hand-written HIP kernels behind a C ABI,
 declared in ``include/rra.h``).  This package is a thin ctypes binding over it;

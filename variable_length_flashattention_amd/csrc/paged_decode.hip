@@ -14,8 +14,13 @@
 // range w is stored in partial slot w + s (two pieces (w, s) and (w', s')
 // with w + s == w' + s' cannot both exist, since ranges and sequences are
 // both in order).  A combine kernel merges the pieces of each sequence and
-// finalizes.  A first tiny kernel writes the group offsets of the sequences
-// (an exclusive prefix sum of ceil(ctx / 16)) into the workspace.
+// finalizes.  The group offsets of the sequences (an exclusive prefix sum
+// of ceil(ctx / 16)) are formed in registers by every wave for up to 256
+// sequences; above that a first one-workgroup kernel writes them into the
+// workspace.  The stateful interface runs the same kernels with each
+// sequence's tokens taken from the tile's block count (cut by a token
+// count), and the combine merging into the caller's (m, l, o) instead of
+// writing out.
 //
 // Per 16 tokens a wave computes
 //   S^T[token][q head] = K . Q^T     (v_mfma_f32_16x16x32_bf16; K straight
@@ -24,8 +29,8 @@
 //   the running reference max by more than 2^8 in probability),
 //   O^T[d][q head] += V^T . P^T      (v_mfma_f32_16x16x16_bf16; V staged in
 //                                     wave-private LDS, read transposed).
-// Only tokens t < context_lens[s] are read; the block table is never read at
-// or past ceil(ctx / block_size).
+// Only tokens t < ctx (the sequence's clamped token count) are read; the
+// block table is never read at or past ceil(ctx / block_size).
 #include "rra_device.h"
 #include "rra_internal.h"
 
