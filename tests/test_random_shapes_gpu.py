@@ -95,3 +95,33 @@ def test_decode_random(seed):
     e = float(np.max(np.abs(got - ref)))
     say(f"  random decode {seed}: max|dout|={e:.3e}")
     assert e <= OUT_TOL
+
+
+@pytest.mark.parametrize("seed", SEEDS[:12])
+def test_decode_steps_random(seed):
+    """The stateful decode over random tiles of blocks equals the oracle's
+    step and finalize."""
+    from oracle_pins import split_into_tiles
+    rng = np.random.Generator(np.random.PCG64(9700 + seed))
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 4, 16]))
+    BS = int(rng.choice([1, 8, 16, 32]))
+    S = int(rng.choice([1, 5, 70, 280]))
+    ctx = rng.integers(0, {1: 2000, 5: 600, 70: 150, 280: 60}[S], size=S)
+    c = I.decode_case(f"srand{seed}", ctx, Hq, Hkv, D, BS, seed=seed)
+    tiles = split_into_tiles(c, rng, max_cap=int(rng.integers(1, 9)))
+    q, kp, vp = dev_bf16(c.q), dev_bf16(c.k_pool), dev_bf16(c.v_pool)
+    say(f"  launch stateful decode seed={seed} S={S} Hq={Hq} Hkv={Hkv} D={D} BS={BS} steps={len(tiles)}")
+    st = rra.decode_state_init(S, Hq, D, "cuda")
+    ref = O.decode_state_init(S, Hq, D)
+    for tb, cnt, tok in tiles:
+        rra.paged_decode_step(st, q, kp, vp, dev_i32(tb), dev_i32(cnt), c.scale, token_counts=dev_i32(tok))
+        O.paged_decode_step(ref, c.q, c.k_pool, c.v_pool, tb, cnt, c.scale, token_counts=tok)
+    out = rra.paged_decode_finalize(st)
+    torch.cuda.synchronize()
+    got, want = host_f64(out), O.paged_decode_finalize(ref)
+    assert np.all(np.isfinite(got))
+    e = float(np.max(np.abs(got - want))) if got.size else 0.0
+    say(f"  random stateful decode {seed}: {len(tiles)} steps, max|dout|={e:.3e}")
+    assert e <= OUT_TOL
