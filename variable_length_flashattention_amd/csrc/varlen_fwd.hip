@@ -242,9 +242,9 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
 #pragma unroll
                 for (int r = 0; r < 16; r++) o[u][dc][r] = 0.f;
         // m_ref: the max the accumulators are currently scaled to; it is only
-        // raised when a row max exceeds it by more than 2^8 in probability
-        // (probabilities stay <= 256, far inside fp32/bf16 range), which
-        // skips most rescales of O.
+        // raised when a tile's probabilities against it grow too large (a
+        // lane's share of a row sum above 2^15), which skips most row-max
+        // reductions and rescales of O.
         float m_ref[RPW], l_run[RPW];
 #pragma unroll
         for (int u = 0; u < RPW; u++) {
@@ -323,35 +323,51 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                             if (key > last) s[u][c][r] = -INFINITY;
                         }
                 }
-                // online softmax (row = this lane's query; lanes l and l^32 share it)
-                float mx = -INFINITY;
+                // online softmax (row = this lane's query; lanes l and l^32 share it).
+                // Probabilities are formed against the reference max m_ref without
+                // looking at this tile's row max; the tile falls back to the
+                // exact max (and rescales O and l) when a row has no reference
+                // yet or this lane's share of the row sum exceeds 2^15 (every
+                // probability then stays <= 2^15, far inside fp32/bf16 range).
+                // l sums the fp32 probabilities (summing their bf16 roundings
+                // would cost lse up to ~2^-9 on rows with few keys).
+                auto probs = [&](float mc) __attribute__((always_inline)) -> float {
+                    float rs = 0.f;
 #pragma unroll
-                for (int c = 0; c < NC; c++)
+                    for (int c = 0; c < NC; c++)
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[u][c][r], s[u][c][r + 1]);
-                mx = max_across_halves(mx);
-                const bool raise = mx > m_ref[u] && (m_ref[u] == -INFINITY || (mx - m_ref[u]) * sl2 > 8.f);
-                if (__builtin_amdgcn_ballot_w64(raise)) {
+                        for (int r2 = 0; r2 < 8; r2++) {
+                            const float p0 = fast_exp2(fmaf(s[u][c][2 * r2], sl2, -mc));
+                            const float p1 = fast_exp2(fmaf(s[u][c][2 * r2 + 1], sl2, -mc));
+                            pk[u][c][r2] = pack_bf16x2(p0, p1);
+                            rs += p0 + p1;
+                        }
+                    return rs;
+                };
+                float rs = 0.f;
+                bool slow = __builtin_amdgcn_ballot_w64(m_ref[u] == -INFINITY) != 0;
+                if (!slow) {
+                    rs = probs(m_ref[u] * sl2);
+                    slow = __builtin_amdgcn_ballot_w64(!(rs <= 32768.f)) != 0;  // (also catches inf)
+                }
+                if (slow) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int c = 0; c < NC; c++)
+#pragma unroll
+                        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[u][c][r], s[u][c][r + 1]);
+                    mx = max_across_halves(mx);
                     const float m_new = fmaxf(m_ref[u], mx);
-                    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_ref[u] - m_new) * sl2);
+                    const float alpha =
+                        (m_ref[u] == -INFINITY || m_new == m_ref[u]) ? 1.f : fast_exp2((m_ref[u] - m_new) * sl2);
                     l_run[u] *= alpha;
 #pragma unroll
                     for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
                         for (int r = 0; r < 16; r++) o[u][dc][r] *= alpha;
                     m_ref[u] = m_new;
+                    rs = probs((m_new == -INFINITY ? 0.f : m_new) * sl2);
                 }
-                const float mc = (m_ref[u] == -INFINITY ? 0.f : m_ref[u]) * sl2;
-                float rs = 0.f;
-#pragma unroll
-                for (int c = 0; c < NC; c++)
-#pragma unroll
-                    for (int r2 = 0; r2 < 8; r2++) {
-                        const float p0 = fast_exp2(fmaf(s[u][c][2 * r2], sl2, -mc));
-                        const float p1 = fast_exp2(fmaf(s[u][c][2 * r2 + 1], sl2, -mc));
-                        pk[u][c][r2] = pack_bf16x2(p0, p1);
-                        rs += p0 + p1;
-                    }
                 l_run[u] += sum_across_halves(rs);
             }
 
