@@ -279,11 +279,13 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             // K fragments are read KD MMAs ahead of use; the scheduling
             // barriers keep the compiler from sinking the reads next to
             // their MMAs (it does that under register pressure, and each
-            // MMA then waits out a full LDS latency).  The wave runs this
-            // phase at raised priority, so that a SIMD shared with a wave in
-            // its softmax keeps issuing these MMAs first (measured: ~3 %
-            // faster on the mixed workload, ~2 % slower on the skewed one).
-            __builtin_amdgcn_s_setprio(1);
+            // MMA then waits out a full LDS latency).  In items of at most
+            // 2048 visible keys the wave runs this phase at raised priority,
+            // so that a SIMD shared with a wave in its softmax keeps issuing
+            // these MMAs first; longer items run faster without it (measured
+            // on gfx950: 16 x U[1,2048] causal 6 % faster with the raise,
+            // 8192-key items 5 % faster without).
+            if (nkt * BK <= 2048) __builtin_amdgcn_s_setprio(1);
             {
                 constexpr int NM = NC * NKS, KD = 3;
                 auto kread = [&](int m) -> bf16x8 {
