@@ -364,24 +364,21 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
 // L = sum l_c 2^{(m_c - M) c}, O = sum o_c 2^{(m_c - M) c}, out = O / L
 // (0 when L == 0, i.e. an empty context).  A step of the stateful interface
 // merges the caller's state (m, l, o) in as one more piece (its m is in
-// scaled units) and stores the merged state instead of out.  One workgroup of NWC waves per
-// (sequence, q head): every wave finds M and L over all pieces (lane-parallel
-// loads), the waves split the o sums, and wave 0 adds their partial sums
-// from LDS.  A piece's o is D floats; LP = D/4 lanes read it as 16-byte
-// pieces, so one wave load covers 64/LP pieces, each lane weighting its own
-// piece (weights are held one piece per lane and fetched with a lane
-// shuffle).
-constexpr int kCombineWaves = 4;
+// scaled units) and stores the merged state instead of out.  One wave per
+// (sequence, q head), four per workgroup, each on its own (no LDS, no
+// barrier): it finds M and L over all pieces (lane-parallel loads) and sums
+// o.  A piece's o is D floats; LP = D/4 lanes read it as 16-byte pieces, so
+// one wave load covers 64/LP pieces, each lane weighting its own piece
+// (weights are held one piece per lane and fetched with a lane shuffle).
 template <int D>
-__global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kernel(DecodeArgs a)
+__global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 {
-    constexpr int NWC = kCombineWaves;
     constexpr int LP = D / 4 < 64 ? D / 4 : 64;   // lanes per piece
     constexpr int PPL = 64 / LP;                   // pieces per wave load
     constexpr int NA = D / LP / 4;                 // 16-byte pieces per lane
-    __shared__ __attribute__((aligned(16))) float part[NWC - 1][D];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t pair = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= (int64_t)a.num_seqs * a.num_q_heads) return;
     const int s = (int)(pair / a.num_q_heads), qh = (int)(pair % a.num_q_heads);
     GroupOffsets go;
     go.init(ctx_source(a), a.ws_goff, a.num_seqs, lane);
@@ -395,9 +392,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     auto slot = [&](int c) -> int64_t { return (int64_t)(w_first + c + s) * a.num_q_heads + qh; };
     const int sub = lane / LP, dl = lane % LP;  // this lane's piece within a load, and d chunk
     // One round trip for the common case: m and l of pieces 0..63 (one per
-    // lane), this wave's first KPRE o loads, and the caller's state max.
+    // lane), the o of the first KPRE*PPL pieces, and the caller's state max.
     // Loads past the last piece read the last piece (weight 0).
-    constexpr int KPRE = 2;
+    constexpr int KPRE = 4;
     const bool stateful = a.st_m != nullptr;
     const float m_prev = stateful ? a.st_m[pair] : -INFINITY;
     float m_c = -INFINITY, l_c = 0.f;
@@ -409,7 +406,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     if (npieces > 0) {
 #pragma unroll
         for (int k = 0; k < KPRE; k++) {
-            const int cc = min(wave * PPL + k * NWC * PPL + sub, npieces - 1);
+            const int cc = min(k * PPL + sub, npieces - 1);
             const float *oc = a.ws_o + slot(cc) * D + 4 * dl;
 #pragma unroll
             for (int i = 0; i < NA; i++) opre[k][i] = *reinterpret_cast<const f32x4 *>(oc + 4 * LP * i);
@@ -420,7 +417,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     // stateful step: the caller's state is one more piece (m in scaled units)
     const float M_s = fmaxf(m_prev, M == -INFINITY ? -INFINITY : M * a.scale);  // merged max, scaled units
-    if (stateful && M_s == -INFINITY) return;  // nothing seen yet and nothing new (uniform in the workgroup)
+    if (stateful && M_s == -INFINITY) return;  // nothing seen yet and nothing new (uniform in the wave)
     const float m_use = stateful ? M_s / a.scale : (M == -INFINITY ? 0.f : M);
     float L = 0.f;
     f32x4 acc[NA];
@@ -436,12 +433,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
             L += (c0 == 0 ? l_c : a.ws_l[slot(c)]) * wgt;
         }
         const int n = min(64, npieces - c0);
-        // this wave's loads: pieces wave*PPL + k*NWC*PPL (+ sub) of the chunk;
-        // in the first chunk the first KPRE of them are already in registers
-        int j = wave * PPL;
+        // pieces j (+ sub), j = 0, PPL, 2 PPL, ... of the chunk; in the first
+        // chunk the first KPRE loads are already in registers
+        int j = 0;
         if (c0 == 0) {
 #pragma unroll
-            for (int k = 0; k < KPRE; k++, j += NWC * PPL) {
+            for (int k = 0; k < KPRE; k++, j += PPL) {
                 const int jj = j + sub;
                 const float wj = __shfl(wgt, jj & 63, 64);
 #pragma unroll
@@ -449,7 +446,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
             }
         }
 #pragma unroll 4
-        for (; j < n; j += NWC * PPL) {
+        for (; j < n; j += PPL) {
             const int jj = j + sub;  // this lane's piece, relative to c0
             const float wj = __shfl(wgt, jj & 63, 64);
             const int cc = min(c0 + jj, npieces - 1);  // (weight 0 past the end)
@@ -469,16 +466,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void paged_decode_combine_kerne
         for (int i = 0; i < NA; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) acc[i][e] += __shfl_xor(acc[i][e], off, 64);
-    if (wave > 0 && sub == 0) {
-#pragma unroll
-        for (int i = 0; i < NA; i++) *reinterpret_cast<f32x4 *>(&part[wave - 1][4 * dl + 4 * LP * i]) = acc[i];
-    }
-    __syncthreads();
-    if (wave == 0 && sub == 0) {
-#pragma unroll
-        for (int w = 0; w < NWC - 1; w++)
-#pragma unroll
-            for (int i = 0; i < NA; i++) acc[i] += *reinterpret_cast<const f32x4 *>(&part[w][4 * dl + 4 * LP * i]);
+    if (sub == 0) {
         if (stateful) {
             const float wp = m_prev == -INFINITY ? 0.f : fast_exp2((m_prev - M_s) * kLog2e);
             float *so = a.st_o + pair * D + 4 * dl;
@@ -602,7 +590,7 @@ static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
     if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, block, 0, stream, a);
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
-    hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)pairs), dim3(64 * kCombineWaves), 0, stream, a);
+    hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
