@@ -85,6 +85,25 @@ def test_scale_and_large_logits():
     compare(out, lse, ro, rl, "peaked")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_logits(causal):
+    """Keys scaled by 2^(j // 128) (exact in bf16): every 128 keys the scores
+    double, so rows keep meeting scores far above their running reference max
+    (probabilities against it overflow the 2^15 bound, and the kernel must fall
+    back to the exact max and rescale O and l), and a second sequence whose
+    keys shrink instead (probabilities against an early max underflow)."""
+    c = I.varlen_case("growing", [700, 300], [700, 300], 2, 128, seed=91, causal=causal)
+    k = I.bf16_to_f32(c.k).astype(np.float64)
+    j = np.arange(700)
+    k[:700] *= (2.0 ** (j // 128))[:, None, None]
+    k[700:] *= (2.0 ** -(np.arange(300) // 64))[:, None, None]
+    c.k = I.bf16_bits(k.astype(np.float32))
+    assert np.array_equal(I.bf16_to_f32(c.k).astype(np.float64), k)  # the scaling is exact
+    out, lse = run_varlen(c)
+    ro, rl = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+    compare(out, lse, ro, rl, f"growing causal={causal}")
+
+
 FULL = [
     ("mixed", lambda causal: I.mixed(causal=causal)),
     ("skewed", lambda causal: I.skewed(causal=causal)),
