@@ -27,6 +27,8 @@
 // Tiles that are read both row-wise (ds_read_b128) and transposed
 // (ds_read_b64_tr_b16) use one XOR swizzle of their 16-byte chunks that is
 // conflict-free enough for both.
+#include <type_traits>
+
 #include "rra_device.h"
 #include "rra_internal.h"
 #include "tile_map.h"
@@ -233,25 +235,34 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void varlen_bwd_dq_kernel(
                     s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(Kb, 32 * c, ks, lane), qf[ks], s[c], 0, 0, 0);
                     dp[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(Vb, 32 * c, ks, lane), gf[ks], dp[c], 0, 0, 0);
                 }
-            // P^T and dS^T (masked pairs give exactly 0)
+            // P^T and dS^T (masked pairs give exactly 0); the mask is applied
+            // only on the tiles that need it (a wave-uniform branch between
+            // two versions of the loop)
             const bool need_mask = (kbase + BK > Lk) || (CAUSAL && kbase + BK - 1 > iw + diag);
             const int last = CAUSAL ? min(Lk - 1, my_i + diag) : Lk - 1;
             uint32_t pk[NC][8];
+            auto probs = [&](auto masked) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-            for (int c = 0; c < NC; c++)
+                for (int c = 0; c < NC; c++)
 #pragma unroll
-                for (int r2 = 0; r2 < 8; r2++) {
-                    float d2[2];
+                    for (int r2 = 0; r2 < 8; r2++) {
+                        float d2[2];
 #pragma unroll
-                    for (int e = 0; e < 2; e++) {
-                        const int r = 2 * r2 + e;
-                        const int key = kbase + 32 * c + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const bool vis = !need_mask || key <= last;
-                        const float p = fast_exp2(s[c][r] * sl2 - lse2);
-                        d2[e] = vis ? p * (dp[c][r] - dsum) : 0.f;
+                        for (int e = 0; e < 2; e++) {
+                            const int r = 2 * r2 + e;
+                            const float p = fast_exp2(s[c][r] * sl2 - lse2);
+                            d2[e] = p * (dp[c][r] - dsum);
+                            if (MASKED) {
+                                const int key = kbase + 32 * c + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                                if (key > last) d2[e] = 0.f;
+                            }
+                        }
+                        pk[c][r2] = pack_bf16x2(d2[0], d2[1]);
                     }
-                    pk[c][r2] = pack_bf16x2(d2[0], d2[1]);
-                }
+            };
+            if (need_mask) probs(std::true_type{});
+            else probs(std::false_type{});
             // dQ^T += K^T dS^T, 16 keys per MMA
 #pragma unroll
             for (int m = 0; m < BK / 16; m++)
@@ -392,28 +403,39 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void varlen_bwd_dkv_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            // P and dS (masked pairs give exactly 0); the mask is applied only
+            // on the tiles that need it (a wave-uniform branch between two
+            // versions of the loop)
             const bool need_mask = (qbase + BQB > Lq) || (kw0 + 32 > Lk) || (CAUSAL && kw0 + 31 > qbase + diag);
             uint32_t pp[8], pd[8];
+            auto probs = [&](auto masked) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                // rows 8j + 4*(lane/32) + 0..3 of the tile
-                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Sb + 8 * j + 4 * (lane >> 5));
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Sb + 32 + 8 * j + 4 * (lane >> 5));
-                float pv[4], dv4[4];
+                for (int j = 0; j < 4; j++) {
+                    // rows 8j + 4*(lane/32) + 0..3 of the tile
+                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Sb + 8 * j + 4 * (lane >> 5));
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Sb + 32 + 8 * j + 4 * (lane >> 5));
+                    float pv[4], dv4[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = 4 * j + e;
-                    const int qi = qbase + 8 * j + 4 * (lane >> 5) + e;
-                    const bool vis = !need_mask || (qi < Lq && my_key < Lk && (!CAUSAL || my_key <= qi + diag));
-                    const float p = fast_exp2(s[r] * sl2 - l4[e]);
-                    pv[e] = vis ? p : 0.f;
-                    dv4[e] = vis ? p * (dp[r] - d4[e]) : 0.f;
+                    for (int e = 0; e < 4; e++) {
+                        const int r = 4 * j + e;
+                        const float p = fast_exp2(s[r] * sl2 - l4[e]);
+                        pv[e] = p;
+                        dv4[e] = p * (dp[r] - d4[e]);
+                        if (MASKED) {
+                            const int qi = qbase + 8 * j + 4 * (lane >> 5) + e;
+                            const bool vis = qi < Lq && my_key < Lk && (!CAUSAL || my_key <= qi + diag);
+                            if (!vis) pv[e] = dv4[e] = 0.f;
+                        }
+                    }
+                    pp[2 * j] = pack_bf16x2(pv[0], pv[1]);
+                    pp[2 * j + 1] = pack_bf16x2(pv[2], pv[3]);
+                    pd[2 * j] = pack_bf16x2(dv4[0], dv4[1]);
+                    pd[2 * j + 1] = pack_bf16x2(dv4[2], dv4[3]);
                 }
-                pp[2 * j] = pack_bf16x2(pv[0], pv[1]);
-                pp[2 * j + 1] = pack_bf16x2(pv[2], pv[3]);
-                pd[2 * j] = pack_bf16x2(dv4[0], dv4[1]);
-                pd[2 * j + 1] = pack_bf16x2(dv4[2], dv4[3]);
-            }
+            };
+            if (need_mask) probs(std::true_type{});
+            else probs(std::false_type{});
             // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per MMA
             {
                 // MMA n: m = n / (2 NDC), dc = n / 2 % NDC, dV (even n) or dK (odd n)
