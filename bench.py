@@ -53,8 +53,10 @@ BWD_SOURCES = ("varlen_bwd.hip", "tile_map.h", "rra_device.h", "rra_internal.h",
 
 
 def kernel_source_hash(files=None):
-    """sha256 prefix over the kernel sources (all of csrc/, or the named files)."""
-    h = hashlib.sha256()
+    """sha256 prefix over the kernel sources (all of csrc/, or the named files)
+    and the compiler flags they are built with."""
+    from variable_length_flashattention_amd import build as B
+    h = hashlib.sha256(" ".join(B.FLAGS).encode())
     csrc = os.path.join(ROOT, "variable_length_flashattention_amd", "csrc")
     for f in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
