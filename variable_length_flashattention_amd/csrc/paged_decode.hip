@@ -445,7 +445,6 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
                 for (int i = 0; i < NA; i++) acc[i] += (jj < n ? wj : 0.f) * opre[k][i];
             }
         }
-#pragma unroll 4
         for (; j < n; j += PPL) {
             const int jj = j + sub;  // this lane's piece, relative to c0
             const float wj = __shfl(wgt, jj & 63, 64);
