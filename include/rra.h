@@ -252,6 +252,35 @@ int32_t rra_paged_decode_finalize(const float *state_l, const float *state_o, vo
                                   int32_t num_q_heads, int32_t head_dim, void *stream);
 
 /*
+ * Padded <-> packed row copies ([PLAN] Goal: a batch of sequences of
+ * different lengths runs packed back to back, addressed by cu_seqlens,
+ * instead of padded to the longest).  They bring a padded batch into the
+ * packed layout the calls above take, and their results back out.
+ *
+ *   padded      [batch, max_seqlen, row]: row t of sequence b at byte
+ *               (b * max_seqlen + t) * row_bytes
+ *   packed      [total, row]: row t of sequence b at byte
+ *               (cu_seqlens[b] + t) * row_bytes
+ *   cu_seqlens  int32 [batch + 1] device array, as for rra_varlen_attn_fwd;
+ *               every length cu[b+1] - cu[b] must be <= max_seqlen (only the
+ *               first max_seqlen rows of a longer sequence are copied)
+ *   row_bytes   bytes per token row, a positive multiple of 4 (e.g.
+ *               num_heads * head_dim * 2 for bf16 q/k/v/out, num_heads * 4
+ *               for fp32 lse); both buffers 4-byte aligned
+ * rra_pack_rows:   packed row cu[b] + t = padded row (b, t) for t < L_b;
+ *                  other packed rows are left untouched.
+ * rra_unpack_rows: padded row (b, t) = packed row cu[b] + t for t < L_b, and
+ *                  all zero bytes for L_b <= t < max_seqlen.
+ * batch == 0 or max_seqlen == 0 is a successful no-op.  The copies are
+ * bit-exact (no arithmetic on the values).
+ */
+int32_t rra_pack_rows(const void *padded, void *packed, const int32_t *cu_seqlens, int32_t batch,
+                      int32_t max_seqlen, int64_t row_bytes, void *stream);
+
+int32_t rra_unpack_rows(const void *packed, void *padded, const int32_t *cu_seqlens, int32_t batch,
+                        int32_t max_seqlen, int64_t row_bytes, void *stream);
+
+/*
  * Test hooks (integer work, checked bit-exactly against an independent
  * definition).
  *
@@ -269,14 +298,23 @@ int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, in
                                   int64_t capacity, int64_t *item_count, void *stream);
 
 /*
- * rra_debug_paged_gather: copies, with the decode kernel's own block-table
- * address computation, every visible pool row into
- * dense[s, t, kh, :] (bf16 [num_seqs, max_blocks_per_seq*block_size, num_kv_heads, head_dim])
- * for t < context_lens[s]; other rows of dense are left untouched.
+ * rra_debug_paged_gather: runs rra_paged_decode_attn's range-split kernel
+ * ([DECODE] step_tile_ref's block-table addressing: token t of sequence s is
+ * slot t % block_size of pool block block_table[s, t / block_size]) in a mode
+ * that keeps everything up to and including its K and V loads -- the same
+ * ranges, pieces, block-table windows, address computation and loads -- and
+ * stores the loaded rows into dense copies instead of computing attention:
+ *   k_dense[s, t, kh, :] = the row its K-operand loads fetched for token t,
+ *   v_dense[s, t, kh, :] = the row its V staging loads fetched for token t,
+ * bf16 [num_seqs, max_blocks_per_seq*block_size, num_kv_heads, head_dim], for
+ * t < context_lens[s]; other rows are left untouched.  The arguments are
+ * those of rra_paged_decode_attn for the same sizes (num_q_heads sets the
+ * range split; the workspace is rra_paged_decode_workspace_bytes of them).
  */
-int32_t rra_debug_paged_gather(const void *pool, const int32_t *block_table, const int32_t *context_lens,
-                               void *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, int32_t max_blocks_per_seq, void *stream);
+int32_t rra_debug_paged_gather(const void *k_pool, const void *v_pool, const int32_t *block_table,
+                               const int32_t *context_lens, void *k_dense, void *v_dense, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -343,6 +343,12 @@ int oracle_varlen_attn_paged(const uint16_t *q, const uint16_t *k_pool, const ui
 /* Everything is recomputed in double from the bf16 inputs (out and lse of  */
 /* the forward are not inputs here).  A row with no visible key has zero    */
 /* gradient; keys that no query sees get dK = dV = 0.                       */
+/*                                                                          */
+/* Given-out variant: the row term sum_j' P_ij' dP_ij' equals dO_i . out_i  */
+/* (out_i = sum_j P_ij v_j), the form a backward pass that takes the        */
+/* forward's stored output uses.  When out_given is passed, the row term is */
+/* that dot product with the given rows (fp64 [Tq, H, D]) instead; with the */
+/* exact out both forms agree to rounding.                                  */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     const uint16_t *q, *k, *v, *dout;
@@ -351,6 +357,7 @@ typedef struct {
     double scale;
     int32_t causal;
     double *dq, *dk, *dv;
+    const double *out_given; /* NULL: the exact row term */
 } bwd_ctx;
 
 /* unit = b*Hkv + kh: every query head of kv head kh, every row of sequence b
@@ -401,6 +408,11 @@ static void bwd_unit(void *p, int64_t unit, double *scratch)
                 dprob[j] = dot;
                 rowdot += prob[j] * dot;
             }
+            if (c->out_given) {
+                const double *orow = c->out_given + ((q0 + i) * H + h) * D;
+                rowdot = 0.0;
+                for (int64_t d = 0; d < D; d++) rowdot += bf16_value(dorow[d]) * orow[d];
+            }
             for (int64_t j = 0; j < Lk; j++) {
                 if (!key_visible(i, j, Lq, Lk, c->causal)) continue;
                 const double ds = prob[j] * (dprob[j] - rowdot);
@@ -416,17 +428,27 @@ static void bwd_unit(void *p, int64_t unit, double *scratch)
         }
 }
 
-int oracle_varlen_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
-                           const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
-                           int32_t num_kv_heads, int32_t head_dim, double scale, int32_t causal,
-                           double *dq, double *dk, double *dv, int32_t nthreads)
+int oracle_varlen_attn_bwd_given_out(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const uint16_t *dout, const double *out_given, const int32_t *cu_q,
+                                     const int32_t *cu_k, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, double scale, int32_t causal, double *dq, double *dk,
+                                     double *dv, int32_t nthreads)
 {
     if (batch < 0 || num_heads <= 0 || head_dim <= 0) return -1;
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
     for (int32_t b = 0; b < batch; b++)
         if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
-    bwd_ctx c = {q, k, v, dout, cu_q, cu_k, num_heads, num_kv_heads, head_dim, scale, causal, dq, dk, dv};
+    bwd_ctx c = {q, k, v, dout, cu_q, cu_k, num_heads, num_kv_heads, head_dim, scale, causal, dq, dk, dv, out_given};
     return run_units(bwd_unit, &c, (int64_t)batch * num_kv_heads, 2 * (size_t)max_len(cu_k, batch) + 1, nthreads);
+}
+
+int oracle_varlen_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                           const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, double scale, int32_t causal,
+                           double *dq, double *dk, double *dv, int32_t nthreads)
+{
+    return oracle_varlen_attn_bwd_given_out(q, k, v, dout, NULL, cu_q, cu_k, batch, num_heads, num_kv_heads,
+                                            head_dim, scale, causal, dq, dk, dv, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

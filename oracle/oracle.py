@@ -47,6 +47,9 @@ def _bind(lib):
     lib.oracle_varlen_attn_bwd.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, f64, i32, f64p,
                                            f64p, f64p, i32]
     lib.oracle_varlen_attn_bwd.restype = ctypes.c_int
+    lib.oracle_varlen_attn_bwd_given_out.argtypes = [u16p, u16p, u16p, u16p, f64p, i32p, i32p, i32, i32, i32, i32,
+                                                     f64, i32, f64p, f64p, f64p, i32]
+    lib.oracle_varlen_attn_bwd_given_out.restype = ctypes.c_int
     lib.oracle_paged_decode.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32, f64, f64p, i32]
     lib.oracle_paged_decode.restype = ctypes.c_int
     lib.oracle_paged_decode_recurrent.argtypes = [u16p, u16p, u16p, i32p, i32p, i32, i32, i32, i32, i32, i32,
@@ -150,10 +153,13 @@ def varlen_attn_paged(q, k_pool, v_pool, cu_q, seqlens_k, block_table, scale, ca
     return out, lse
 
 
-def varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, scale, causal, nthreads=None, lib=None):
+def varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, scale, causal, out=None, nthreads=None, lib=None):
     """Gradients of sum(out * dout) of the packed forward pass: q, dout
     [Tq,H,D], k, v [Tk,Hkv,D] bf16 bits.  Returns (dq [Tq,H,D], dk [Tk,Hkv,D],
-    dv [Tk,Hkv,D]) float64; rows outside every sequence stay NaN."""
+    dv [Tk,Hkv,D]) float64; rows outside every sequence stay NaN.  With
+    ``out`` (float64 [Tq,H,D], e.g. a rounded forward output) the softmax
+    Jacobian's row term is dout_i . out_i from those rows instead of its
+    exact value."""
     lib = lib or load()
     q, k, v, dout = (_c(x, np.uint16) for x in (q, k, v, dout))
     cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
@@ -162,8 +168,16 @@ def varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, scale, causal, nthreads=None, lib
     dq = np.full((Tq, H, D), np.nan)
     dk = np.full((Tk, Hkv, D), np.nan)
     dv = np.full((Tk, Hkv, D), np.nan)
-    rc = lib.oracle_varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, len(cu_q) - 1, H, Hkv, D, float(scale),
-                                    int(bool(causal)), dq, dk, dv, nthreads or default_threads())
+    if out is None:
+        rc = lib.oracle_varlen_attn_bwd(q, k, v, dout, cu_q, cu_k, len(cu_q) - 1, H, Hkv, D, float(scale),
+                                        int(bool(causal)), dq, dk, dv, nthreads or default_threads())
+    else:
+        out = _c(out, np.float64)
+        if out.shape != (Tq, H, D):
+            raise ValueError("out must be float64 [Tq, H, D]")
+        rc = lib.oracle_varlen_attn_bwd_given_out(q, k, v, dout, out, cu_q, cu_k, len(cu_q) - 1, H, Hkv, D,
+                                                  float(scale), int(bool(causal)), dq, dk, dv,
+                                                  nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_varlen_attn_bwd rejected its arguments")
     return dq, dk, dv

@@ -69,26 +69,3 @@ def compare(out, lse, ref_out, ref_lse, what):
     assert eo <= OUT_TOL, f"{what}: max|dout| {eo}"
     assert el <= LSE_TOL, f"{what}: max|dlse| {el}"
     return eo, el
-
-
-def sample_rows(case, n_random=256, seed=0):
-    """(token, head) rows to check at full size: the first and last row of each
-    sequence, rows on both sides of each 128-row tile edge, and random rows."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    H = case.num_heads
-    toks = set()
-    for b in range(case.batch):
-        s, e = int(case.cu_q[b]), int(case.cu_q[b + 1])
-        if e == s:
-            continue
-        toks.update([s, e - 1])
-        for edge in range(128, e - s, 128):
-            toks.update([s + edge - 1, s + edge])
-    toks = sorted(toks)
-    if len(toks) > 400:
-        toks = list(rng.choice(toks, size=400, replace=False))
-    Tq = int(case.cu_q[-1])
-    toks += list(rng.integers(0, Tq, size=n_random))
-    heads = rng.integers(0, H, size=len(toks))
-    rows = np.stack([np.asarray(toks, np.int64), heads], axis=1).astype(np.int32)
-    return np.unique(rows, axis=0)

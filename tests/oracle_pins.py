@@ -424,6 +424,63 @@ def pin_backward(lib):
                 assert abs(fd - g[idx]) <= 1e-6 * (1 + abs(fd)), f"finite difference {which} {idx}: {fd} vs {g[idx]}"
 
 
+def _softmax_probs(q, k, cu_q, cu_k, scale, causal):
+    """Dense per-sequence probabilities P[b] (numpy float64, [H, Lq, Lk],
+    rows without a visible key all 0), straight from the definition."""
+    qf, kf = bf16_to_f32(q).astype(np.float64), bf16_to_f32(k).astype(np.float64)
+    R = qf.shape[1] // kf.shape[1]
+    probs = []
+    for b in range(len(cu_q) - 1):
+        qs, ks = qf[cu_q[b]:cu_q[b + 1]], np.repeat(kf[cu_k[b]:cu_k[b + 1]], R, axis=1)
+        Lq, Lk = qs.shape[0], ks.shape[0]
+        s = scale * np.einsum("ihd,jhd->hij", qs, ks)
+        vis = (np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + Lk - Lq) if causal else np.ones((Lq, Lk), bool)
+        s = np.where(vis[None], s, -np.inf)
+        m = np.max(s, axis=2, keepdims=True) if Lk else np.zeros((qs.shape[1], Lq, 1))
+        m = np.where(np.isfinite(m), m, 0.0)
+        e = np.exp(s - m)
+        z = e.sum(axis=2, keepdims=True)
+        probs.append(np.divide(e, z, out=np.zeros_like(e), where=z > 0))
+    return probs
+
+
+def pin_backward_given_out(lib):
+    """The backward with the softmax Jacobian's row term taken from a given
+    out: (1) with the exact forward out it equals the exact gradients
+    (dO_i . out_i = sum_j P_ij dP_ij) within 1e-12; (2) with out + delta it
+    differs from them by the closed form of a shifted row term:
+    dq_i -= scale (dO_i . delta_i) sum_j P_ij k_j, dk_j -= scale sum_i P_ij
+    (dO_i . delta_i) q_i, and dv is unchanged (it has no row term)."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    for trial, (H, Hkv) in enumerate([(2, 2), (4, 2), (3, 1)]):
+        c = _random_case(rng, B=int(rng.integers(1, 4)), H=H, D=8, max_len=8, Hkv=Hkv)
+        dout = normal_bf16_like(rng, c.q.shape)
+        for causal in (False, True):
+            exact = O.varlen_attn_bwd(c.q, c.k, c.v, dout, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+            out, _ = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, lib=lib)
+            out0 = np.nan_to_num(out)
+            same = O.varlen_attn_bwd(c.q, c.k, c.v, dout, c.cu_q, c.cu_k, c.scale, causal, out=out0, lib=lib)
+            for name, a, b in zip(("dq", "dk", "dv"), same, exact):
+                _close(a, b, 1e-12, f"given exact out, {name}, trial {trial} causal {causal}")
+            delta = rng.standard_normal(out0.shape)
+            shifted = O.varlen_attn_bwd(c.q, c.k, c.v, dout, c.cu_q, c.cu_k, c.scale, causal, out=out0 + delta,
+                                        lib=lib)
+            gf = bf16_to_f32(dout).astype(np.float64)
+            qf, kf = bf16_to_f32(c.q).astype(np.float64), bf16_to_f32(c.k).astype(np.float64)
+            R = H // Hkv
+            want_dq, want_dk = exact[0].copy(), exact[1].copy()
+            for b, P in enumerate(_softmax_probs(c.q, c.k, c.cu_q, c.cu_k, c.scale, causal)):
+                qs, qe, ks, ke = c.cu_q[b], c.cu_q[b + 1], c.cu_k[b], c.cu_k[b + 1]
+                t = np.einsum("ihd,ihd->hi", gf[qs:qe], delta[qs:qe])          # dO_i . delta_i, [H, Lq]
+                kr = np.repeat(kf[ks:ke], R, axis=1)                            # [Lk, H, D]
+                want_dq[qs:qe] -= c.scale * np.einsum("hi,hij,jhd->ihd", t, P, kr)
+                dk_h = c.scale * np.einsum("hij,hi,ihd->jhd", P, t, qf[qs:qe])  # per query head
+                want_dk[ks:ke] -= dk_h.reshape(ke - ks, Hkv, R, c.head_dim).sum(axis=2)
+            _close(shifted[0], want_dq, 1e-11, f"shifted out, dq, trial {trial} causal {causal}")
+            _close(shifted[1], want_dk, 1e-11, f"shifted out, dk, trial {trial} causal {causal}")
+            _close(shifted[2], exact[2], 1e-12, f"shifted out, dv, trial {trial} causal {causal}")
+
+
 def normal_bf16_like(rng, shape):
     return bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
 
@@ -611,6 +668,7 @@ ALL_PINS = [
     pin_gqa_prefill,
     pin_paged_prefill,
     pin_backward,
+    pin_backward_given_out,
     pin_decode_direct_equals_recurrence,
     pin_decode_equals_varlen_single_query,
     pin_decode_step,

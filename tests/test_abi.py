@@ -77,8 +77,10 @@ def varlen_status(lib, **kw):
     (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
     (dict(D=96), 2), (dict(D=512), 2), (dict(D=32), 2),
     (dict(q=None), 1), (dict(out=None), 1), (dict(lse=None), 1), (dict(cuq=None), 1), (dict(cuk=None), 1),
+    (dict(k=None), 1), (dict(v=None), 1), (dict(k=None, v=None), 1),
     (dict(q=FAKE + 2), 1), (dict(out=FAKE + 8), 1), (dict(k=FAKE + 4), 1),
     (dict(batch=0), 0), (dict(maxq=0), 0), (dict(batch=0, q=None, out=None), 0),
+    (dict(batch=0, k=None, v=None), 0), (dict(maxq=0, k=None, v=None), 0),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen_status(lib, **kw) == status
@@ -96,6 +98,7 @@ def varlen_gqa_status(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(Hkv=0), 1), (dict(Hkv=-2), 1), (dict(Hkv=3), 1), (dict(H=8, Hkv=16), 1), (dict(H=0), 1),
     (dict(D=96), 2), (dict(k=FAKE + 2), 1), (dict(batch=0), 0), (dict(maxq=0, Hkv=3), 1),
+    (dict(k=None), 1), (dict(v=None), 1),
 ])
 def test_varlen_gqa_validation(lib, kw, status):
     assert varlen_gqa_status(lib, **kw) == status
@@ -165,8 +168,9 @@ def decode_status(lib, **kw):
     (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(D=0), 1),
     (dict(D=80), 2), (dict(BS=12), 2), (dict(BS=2048), 2),
     (dict(q=None), 1), (dict(out=None), 1), (dict(bt=None), 1), (dict(cl=None), 1), (dict(q=FAKE + 2), 1),
+    (dict(kp=None), 1), (dict(vp=None), 1), (dict(kp=None, vp=None), 1),
     (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=FAKE + 4), 3),
-    (dict(S=0), 0), (dict(S=0, q=None, ws=None), 0),
+    (dict(S=0), 0), (dict(S=0, q=None, ws=None), 0), (dict(S=0, kp=None, vp=None), 0),
 ])
 def test_decode_validation(lib, kw, status):
     assert decode_status(lib, **kw) == status
@@ -186,7 +190,7 @@ def step_status(lib, **kw):
     (dict(scale=-0.5), 1), (dict(scale=float("inf")), 1),
     (dict(D=96), 2), (dict(BS=24), 2),
     (dict(m=None), 1), (dict(l=None), 1), (dict(o=None), 1), (dict(o=FAKE + 4), 1), (dict(tb=None), 1),
-    (dict(tc=None), 1), (dict(q=None), 1), (dict(kp=FAKE + 2), 1),
+    (dict(tc=None), 1), (dict(q=None), 1), (dict(kp=FAKE + 2), 1), (dict(kp=None), 1), (dict(vp=None), 1),
     (dict(ws=None), 3), (dict(wsb=64), 3),
     (dict(S=0), 0), (dict(S=0, m=None, l=None, o=None, ws=None), 0),
 ])
@@ -239,3 +243,16 @@ def test_debug_tile_map_validation(lib):
     assert st == 2
     st = lib.rra_debug_varlen_tile_map(FAKE, 0, 2, 100, 128, None, 0, ctypes.byref(count), None)
     assert st == 0 and count.value == 0
+
+
+@pytest.mark.parametrize("fn", ["rra_pack_rows", "rra_unpack_rows"])
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, -1, 8, 16), 1), ((FAKE, FAKE, FAKE, 2, -1, 16), 1), ((FAKE, FAKE, FAKE, 2, 8, 0), 1),
+    ((FAKE, FAKE, FAKE, 2, 8, 6), 1), ((FAKE, FAKE, FAKE, 2, 8, -4), 1),
+    ((None, FAKE, FAKE, 2, 8, 16), 1), ((FAKE, None, FAKE, 2, 8, 16), 1), ((FAKE, FAKE, None, 2, 8, 16), 1),
+    ((FAKE + 2, FAKE, FAKE, 2, 8, 16), 1), ((FAKE, FAKE + 1, FAKE, 2, 8, 16), 1),
+    ((FAKE, FAKE, FAKE, 1 << 30, 1 << 30, 4), 1),
+    ((None, None, None, 0, 8, 16), 0), ((None, None, None, 2, 0, 16), 0),
+])
+def test_pack_rows_validation(lib, fn, args, status):
+    assert getattr(lib, fn)(*args, None) == status

@@ -47,15 +47,65 @@ def test_tile_map_configs():
         assert np.array_equal(got[:len(ref)], ref) and np.all(got[len(ref):] == -1), c.name
 
 
-@pytest.mark.parametrize("ctx,BS,Hkv,D", [
-    ([5, 0, 37, 16, 17], 16, 2, 128), ([1, 2, 3, 100], 1, 1, 64), ([300, 9], 8, 4, 256), ([1000, 64], 32, 2, 128),
-])
-def test_gather_bit_exact(ctx, BS, Hkv, D):
-    c = I.decode_case("g", ctx, Hkv, Hkv, D, BS, seed=sum(ctx))
-    dense = torch.full((c.num_seqs, c.max_blocks * BS, Hkv, D), -1, dtype=torch.int16, device="cuda")
-    say(f"  launch rra_debug_paged_gather ctx={ctx} BS={BS} Hkv={Hkv} D={D}")
-    rra.rra_debug_paged_gather(dev_bf16(c.k_pool), dev_i32(c.block_table), dev_i32(c.context_lens), dense,
-                               c.num_seqs, Hkv, D, BS, c.max_blocks)
-    got = dense.cpu().numpy().view(np.uint16)
-    ref = O.paged_gather(c.k_pool, c.block_table, c.context_lens, fill=0xFFFF)
-    assert np.array_equal(got, ref)
+def device_gather(c, Hq):
+    """Run the decode split kernel in its gather mode through the C ABI;
+    returns (k_dense, v_dense) as uint16 arrays, unwritten rows 0xFFFF."""
+    S, BS, Hkv, D = c.num_seqs, c.block_size, c.num_kv_heads, c.head_dim
+    shape = (S, c.max_blocks * BS, Hkv, D)
+    kd = torch.full(shape, -1, dtype=torch.int16, device="cuda")
+    vd = torch.full(shape, -1, dtype=torch.int16, device="cuda")
+    need = rra.rra_paged_decode_workspace_bytes(S, Hq, Hkv, D)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    say(f"  launch rra_debug_paged_gather S={S} Hq={Hq} Hkv={Hkv} D={D} BS={BS} max_blocks={c.max_blocks} "
+        f"max_ctx={int(c.context_lens.max())}")
+    rra.rra_debug_paged_gather(dev_bf16(c.k_pool), dev_bf16(c.v_pool), dev_i32(c.block_table),
+                               dev_i32(c.context_lens), kd, vd, S, Hq, Hkv, D, BS, c.max_blocks, ws, ws.numel())
+    torch.cuda.synchronize()
+    return kd.cpu().numpy().view(np.uint16), vd.cpu().numpy().view(np.uint16)
+
+
+def check_gather(c, Hq):
+    kd, vd = device_gather(c, Hq)
+    assert np.array_equal(kd, O.paged_gather(c.k_pool, c.block_table, c.context_lens, fill=0xFFFF)), "K loads"
+    assert np.array_equal(vd, O.paged_gather(c.v_pool, c.block_table, c.context_lens, fill=0xFFFF)), "V loads"
+
+
+# Block sizes below 16 hold 4 table entries per lane (windows of 256 blocks;
+# entries 64 and up are fetched from the second to fourth register), 16 and
+# above one per lane (windows of 64 blocks).  Contexts longer than one window
+# make a piece span several windows.
+GATHER_CASES = [
+    # ctx, BS, Hq, Hkv, D
+    ([5, 0, 37, 16, 17], 16, 2, 2, 128),
+    ([1, 2, 3, 100], 1, 1, 1, 64),
+    ([300, 9, 70, 1], 1, 4, 2, 128),          # 300 blocks: rel >= 64, >= 128, >= 192 and a second window
+    ([1100, 3, 257, 1024], 4, 8, 2, 64),      # 275 blocks of 4
+    ([600, 513, 4, 2100], 8, 4, 4, 256),      # 75 and 263 blocks of 8
+    ([300, 9], 8, 8, 4, 256),
+    ([1000, 64, 4097, 1], 16, 32, 8, 128),    # 257 blocks of 16: five windows of 64
+    ([5000, 63, 64, 65, 1], 64, 16, 2, 64),   # 79 blocks of 64
+    ([1000, 64], 32, 2, 2, 128),
+]
+
+
+@pytest.mark.parametrize("ctx,BS,Hq,Hkv,D", GATHER_CASES)
+def test_gather_bit_exact(ctx, BS, Hq, Hkv, D):
+    c = I.decode_case("g", ctx, Hq, Hkv, D, BS, seed=sum(ctx) + BS)
+    check_gather(c, Hq)
+
+
+def test_gather_many_sequences():
+    """More sequences than the split kernel keeps offsets for in registers:
+    the offsets kernel writes them into the workspace and waves search them."""
+    rng = np.random.Generator(np.random.PCG64(4242))
+    ctx = rng.integers(0, 200, size=700)
+    for BS in (4, 16):
+        c = I.decode_case("g_many", ctx, 8, 2, 128, BS, seed=4243 + BS)
+        check_gather(c, 8)
+
+
+def test_gather_decode_workload():
+    """The paged decode workload at full size (64 sequences, contexts U[1,8192],
+    Hq=32, Hkv=8, head_dim 128, 16-token blocks), in the benchmark's launch
+    configuration: every K and V row the split kernel loads, bit for bit."""
+    check_gather(I.paged_decode(), 32)

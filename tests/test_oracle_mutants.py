@@ -56,6 +56,9 @@ MUTANTS = [
      "for (int64_t h = kh * R; h < kh * R + 1; h++)"),
     ("bwd_unnormalised_probs", "prob[j] = prob[j] == -INFINITY ? 0.0 : exp(prob[j] - M) / Z;",
      "prob[j] = prob[j] == -INFINITY ? 0.0 : exp(prob[j] - M);"),
+    ("bwd_given_out_ignored",
+     "rowdot = 0.0;\n                for (int64_t d = 0; d < D; d++) rowdot += bf16_value(dorow[d]) * orow[d];",
+     "(void)orow;"),
     ("tile_levels_ascending", "for (int64_t r = max_tiles - 1; r >= 0; r--) {", "for (int64_t r = 0; r < max_tiles; r++) {"),
     ("tile_count_floor", "const int64_t n = (L + block_q - 1) / block_q;\n            if (n <= r) continue;",
      "const int64_t n = L / block_q;\n            if (n <= r) continue;"),

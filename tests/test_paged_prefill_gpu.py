@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 import variable_length_flashattention_amd as rra
-from gpu_helpers import compare, dev_bf16, dev_i32, host_f64, run_varlen, sample_rows, say
+from gpu_helpers import compare, dev_bf16, dev_i32, host_f64, run_varlen, say
 from variable_length_flashattention_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -69,20 +69,15 @@ def test_paged_table_with_spare_columns():
 @pytest.mark.parametrize("block_size", [16, 256])
 def test_chunked_full_size(block_size):
     """The skewed/chunked shape (Lq {8192,1024,128,7}, Lk {8192,3072,128,519},
-    16 heads, head_dim 128, bottom-right causal) with paged K/V: every row
-    written and finite (the pool's unused slots hold NaN), bit for bit the
-    packed forward pass on the same K/V, and sampled rows against the
-    oracle."""
+    16 heads, head_dim 128, bottom-right causal) with paged K/V (the pool's
+    unused slots hold NaN): bit for bit the packed forward pass on the same
+    K/V, and every (token, head) row against the oracle."""
     c = I.chunked_paged(block_size)
     out, lse = run_paged(c)
-    assert np.all(np.isfinite(out)) and not np.any(np.isnan(lse)), "unwritten or NaN rows"
     pout, plse = run_varlen(c.dense, causal=True)
     assert np.array_equal(out, pout) and np.array_equal(lse, plse), "paged differs from packed"
-    rows = sample_rows(c.dense)
-    ro, rl = O.varlen_attn_paged(c.q, c.k_pool, c.v_pool, c.cu_q, c.seqlens_k, c.block_table, c.scale, True,
-                                 rows=rows)
-    compare(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl,
-            f"chunked paged bs{block_size} rows={len(rows)}")
+    ro, rl = O.varlen_attn_paged(c.q, c.k_pool, c.v_pool, c.cu_q, c.seqlens_k, c.block_table, c.scale, True)
+    compare(out, lse, ro, rl, f"chunked paged bs{block_size}, every row")
 
 
 def test_paged_convenience_wrapper():

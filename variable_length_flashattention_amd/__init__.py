@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     rra_paged_decode_state_init,
     rra_paged_decode_step,
     rra_paged_decode_finalize,
+    rra_pack_rows,
+    rra_unpack_rows,
     rra_debug_varlen_tile_map,
     rra_debug_paged_gather,
     varlen_attn_fwd,
@@ -30,4 +32,6 @@ from .binding import (  # noqa: F401
     decode_state_init,
     paged_decode_step,
     paged_decode_finalize,
+    pack_padded,
+    unpack_to_padded,
 )

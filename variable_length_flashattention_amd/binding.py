@@ -12,6 +12,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "librra.so"
 _lib = None
@@ -72,9 +74,13 @@ def load_library():
     lib.rra_paged_decode_finalize.restype = i32
     lib.rra_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.rra_paged_decode_workspace_bytes.restype = sz
+    lib.rra_pack_rows.argtypes = [vp, vp, vp, i32, i32, i64, vp]
+    lib.rra_pack_rows.restype = i32
+    lib.rra_unpack_rows.argtypes = [vp, vp, vp, i32, i32, i64, vp]
+    lib.rra_unpack_rows.restype = i32
     lib.rra_debug_varlen_tile_map.argtypes = [vp, i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64), vp]
     lib.rra_debug_varlen_tile_map.restype = i32
-    lib.rra_debug_paged_gather.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.rra_debug_paged_gather.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.rra_debug_paged_gather.restype = i32
     _lib = lib
     return lib
@@ -201,11 +207,25 @@ def rra_debug_varlen_tile_map(cu_seqlens_q, batch, num_heads, max_seqlen_q, head
     return int(count.value)
 
 
-def rra_debug_paged_gather(pool, block_table, context_lens, dense, num_seqs, num_kv_heads, head_dim, block_size,
-                           max_blocks_per_seq, stream=None):
+def rra_pack_rows(padded, packed, cu_seqlens, batch, max_seqlen, row_bytes, stream=None):
+    st = load_library().rra_pack_rows(_ptr(padded), _ptr(packed), _ptr(cu_seqlens), int(batch), int(max_seqlen),
+                                      int(row_bytes), _stream(stream))
+    _check("rra_pack_rows", st)
+
+
+def rra_unpack_rows(packed, padded, cu_seqlens, batch, max_seqlen, row_bytes, stream=None):
+    st = load_library().rra_unpack_rows(_ptr(packed), _ptr(padded), _ptr(cu_seqlens), int(batch), int(max_seqlen),
+                                        int(row_bytes), _stream(stream))
+    _check("rra_unpack_rows", st)
+
+
+def rra_debug_paged_gather(k_pool, v_pool, block_table, context_lens, k_dense, v_dense, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, max_blocks_per_seq, workspace, workspace_bytes,
+                           stream=None):
     st = load_library().rra_debug_paged_gather(
-        _ptr(pool), _ptr(block_table), _ptr(context_lens), _ptr(dense), int(num_seqs), int(num_kv_heads),
-        int(head_dim), int(block_size), int(max_blocks_per_seq), _stream(stream))
+        _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens), _ptr(k_dense), _ptr(v_dense),
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_blocks_per_seq), _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("rra_debug_paged_gather", st)
 
 
@@ -261,6 +281,36 @@ def varlen_attn_bwd(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seq
                         max_seqlen_k, cu_seqlens_q.numel() - 1, H, k.shape[1], D, softmax_scale, causal, workspace,
                         workspace.numel() * workspace.element_size(), stream)
     return dq, dk, dv
+
+
+def pack_padded(padded, cu_seqlens, total=None, stream=None):
+    """padded [B, Lmax, ...] device tensor, cu_seqlens int32 [B+1] device
+    tensor -> packed [total, ...] (total = cu_seqlens[-1], read on the host
+    when not given)."""
+    import torch
+    if not padded.is_contiguous() or not padded.is_cuda:
+        raise ValueError("padded must be a contiguous device tensor")
+    B, Lmax = padded.shape[:2]
+    if cu_seqlens.numel() != B + 1:
+        raise ValueError("cu_seqlens must have batch + 1 entries")
+    total = int(cu_seqlens[-1].item()) if total is None else int(total)
+    packed = torch.empty((total,) + tuple(padded.shape[2:]), dtype=padded.dtype, device=padded.device)
+    row_bytes = padded[0, 0].numel() * padded.element_size() if Lmax and B else 4
+    rra_pack_rows(padded, packed, cu_seqlens, B, Lmax, row_bytes, stream)
+    return packed
+
+
+def unpack_to_padded(packed, cu_seqlens, max_seqlen, stream=None):
+    """packed [total, ...] device tensor -> padded [B, max_seqlen, ...]
+    (rows past each sequence's length are zero)."""
+    import torch
+    if not packed.is_contiguous() or not packed.is_cuda:
+        raise ValueError("packed must be a contiguous device tensor")
+    B = cu_seqlens.numel() - 1
+    padded = torch.empty((B, int(max_seqlen)) + tuple(packed.shape[1:]), dtype=packed.dtype, device=packed.device)
+    row_bytes = max(1, int(np.prod(packed.shape[1:], dtype=np.int64))) * packed.element_size()
+    rra_unpack_rows(packed, padded, cu_seqlens, B, int(max_seqlen), row_bytes, stream)
+    return padded
 
 
 def varlen_attn_fwd_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q, softmax_scale,

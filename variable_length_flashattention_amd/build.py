@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["rra_api.hip", "varlen_fwd.hip", "varlen_bwd.hip", "paged_decode.hip"]
+SOURCES = ["rra_api.hip", "varlen_fwd.hip", "varlen_bwd.hip", "paged_decode.hip", "pack_rows.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -38,16 +38,6 @@ namespace rra {
 
 constexpr int kGroup = 16;  // tokens per MMA step
 
-// Element offset of (token t, kv head kh) of a sequence whose block-table row
-// is bt.  block_size = 1 << bs_shift.
-__device__ __forceinline__ int64_t paged_token_offset(const int32_t *__restrict__ bt, int t, int bs_shift,
-                                                      int num_kv_heads, int head_dim, int kh)
-{
-    const int64_t blk = bt[t >> bs_shift];
-    const int64_t slot = t & ((1 << bs_shift) - 1);
-    return ((blk << bs_shift) + slot) * num_kv_heads * head_dim + (int64_t)kh * head_dim;
-}
-
 // Context length as the kernels use it: clamped to [0, max_blocks * block_size]
 // so that no block-table entry past the row is read.
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int bs_shift)
@@ -176,7 +166,12 @@ struct GroupOffsets {
 
 // BIG: block_size >= 16, so each group of 16 tokens sits in one pool block
 // and its block id is wave-uniform.
-template <int D, bool BIG>
+// GATHER: the test hook's mode.  The kernel walks the same ranges, pieces,
+// block-table windows and groups and issues the same K and V loads, then
+// stores the loaded registers into dense copies (a.gather_k, a.gather_v
+// [S, max_blocks * block_size, Hkv, D]) at the positions the operand layouts
+// assign them, instead of folding them into a softmax state.
+template <int D, bool BIG, bool GATHER>
 __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
 {
     constexpr int NKS = D / 32;   // k-steps of the QK^T MMA (32 d each)
@@ -222,7 +217,7 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
 
         // Q^T operand: lane holds Q[qh0 + col][32*ks + 8*grp .. +7]
         bf16x8 qf[NKS];
-        {
+        if constexpr (!GATHER) {
             const uint16_t *qrow = a.q + ((int64_t)s * a.num_q_heads + qh0 + (q_ok ? col : 0)) * D + 8 * grp;
 #pragma unroll
             for (int ks = 0; ks < NKS; ks++) qf[ks] = as_bf16x8(load16(qrow + 32 * ks));
@@ -330,20 +325,48 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
                 }
             };
 
+            // GATHER: store a group's loaded registers where the operand
+            // layouts place them: K lane (col, grp) holds token t0 + col,
+            // d = 32*ks + 8*grp..+7; V piece c = lane + 64 i holds token
+            // t0 + c/(D/8), d = 8*(c%(D/8))..+7.  Tokens at or past t_end
+            // (re-reads of token t_end-1) are not stored.
+            auto scatter = [&](int t0, const u32x4 *kr, const u32x4 *vr) {
+                const int64_t T = (int64_t)a.max_blocks << bs_shift;  // dense rows per sequence
+                const int tk = t0 + col;
+                if (tk < t_end) {
+                    uint16_t *dk = a.gather_k + (((int64_t)s * T + tk) * Hkv + kh) * D + 8 * grp;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ks++) *reinterpret_cast<u32x4 *>(dk + 32 * ks) = kr[ks];
+                }
+#pragma unroll
+                for (int i = 0; i < NV; i++) {
+                    const int c = lane + 64 * i;
+                    const int tv = t0 + c / (D / 8);
+                    if (tv < t_end)
+                        *reinterpret_cast<u32x4 *>(a.gather_v + (((int64_t)s * T + tv) * Hkv + kh) * D +
+                                                   8 * (c % (D / 8))) = vr[i];
+                }
+            };
+            auto consume = [&](int t0, const u32x4 *kr, const u32x4 *vr, uint16_t *vb) {
+                if constexpr (GATHER) scatter(t0, kr, vr);
+                else process(t0, kr, vr, vb);
+            };
+
             // Two register sets alternate (no copies between them), so the
             // loads of the next group are in flight while this one is processed.
             u32x4 ka[NKS], va_[NV], kb[NKS], vb_[NV];
             load_group(c_begin, ka, va_);
             for (int t0 = c_begin; t0 < t_end; t0 += 2 * kGroup) {
                 if (t0 + kGroup < t_end) load_group(t0 + kGroup, kb, vb_);
-                process(t0, ka, va_, vbuf[wave][0]);
+                consume(t0, ka, va_, vbuf[wave][0]);
                 if (t0 + kGroup >= t_end) break;
                 if (t0 + 2 * kGroup < t_end) load_group(t0 + 2 * kGroup, ka, va_);
-                process(t0 + kGroup, kb, vb_, vbuf[wave][1]);
+                consume(t0 + kGroup, kb, vb_, vbuf[wave][1]);
             }
             c_begin = t_end;
         }
 
+        if constexpr (GATHER) continue;
         // this piece's partial state (unnormalised o, l, and the reference max)
         float l_run = l_part + __shfl_xor(l_part, 16, 64);
         l_run += __shfl_xor(l_run, 32, 64);
@@ -539,25 +562,6 @@ hipError_t launch_decode_state_init(float *state_m, float *state_l, float *state
     return hipGetLastError();
 }
 
-// Test hook: the split kernel's address computation, as a plain copy.
-__global__ __launch_bounds__(256) void paged_gather_kernel(const uint16_t *pool, const int32_t *block_table,
-                                                           const int32_t *context_lens, uint16_t *dense,
-                                                           int32_t num_kv_heads, int32_t head_dim, int32_t bs_shift,
-                                                           int32_t max_blocks)
-{
-    const int s = blockIdx.y, t = blockIdx.x;
-    if (t >= context_lens[s]) return;
-    const int32_t *bt = block_table + (int64_t)s * max_blocks;
-    const int chunks = num_kv_heads * head_dim / 8;
-    const int64_t T = (int64_t)max_blocks << bs_shift;
-    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-        const int kh = c / (head_dim / 8), cc = c % (head_dim / 8);
-        const uint16_t *src = pool + paged_token_offset(bt, t, bs_shift, num_kv_heads, head_dim, kh) + cc * 8;
-        uint16_t *dst = dense + (((int64_t)s * T + t) * num_kv_heads + kh) * head_dim + cc * 8;
-        *reinterpret_cast<u32x4 *>(dst) = load16(src);
-    }
-}
-
 // Ranges of token groups: enough waves for one full round on a 256-CU device
 // (256 CUs x 4 SIMDs x the split kernel's waves per SIMD: 4, 2 and 1 at
 // head_dim 64, 128 and 256), spread over the kv-head units.
@@ -578,16 +582,22 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
     return up(goff) + up(2 * n * sizeof(float)) + n * (size_t)head_dim * sizeof(float);
 }
 
-template <int D>
-static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
+template <int D, bool GATHER>
+static void launch_split(const DecodeArgs &a, hipStream_t stream)
 {
     if (a.num_seqs > kRegSeqs)
         hipLaunchKernelGGL(paged_decode_offsets_kernel, dim3(1), dim3(256), 0, stream, ctx_source(a), a.num_seqs,
                            a.ws_goff);
     const int64_t units = (int64_t)a.num_kv_heads * a.n_sub;
     const dim3 grid((unsigned)a.n_ranges, (unsigned)((units + 3) / 4)), block(256);
-    if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, block, 0, stream, a);
+    if (a.bs_shift >= 4) hipLaunchKernelGGL((paged_decode_split_kernel<D, true, GATHER>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((paged_decode_split_kernel<D, false, GATHER>), grid, block, 0, stream, a);
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
+{
+    launch_split<D, false>(a, stream);
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
     hipLaunchKernelGGL(paged_decode_combine_kernel<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -603,14 +613,14 @@ hipError_t launch_paged_decode(const DecodeArgs &a, int head_dim, hipStream_t st
     }
 }
 
-hipError_t launch_paged_gather(const uint16_t *pool, const int32_t *block_table, const int32_t *context_lens,
-                               uint16_t *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, int32_t bs_shift, int32_t max_blocks, hipStream_t stream)
+hipError_t launch_paged_gather(const DecodeArgs &a, int head_dim, hipStream_t stream)
 {
-    const int64_t T = (int64_t)max_blocks * block_size;
-    if (T == 0 || num_seqs == 0) return hipSuccess;
-    hipLaunchKernelGGL(paged_gather_kernel, dim3((unsigned)T, (unsigned)num_seqs), dim3(256), 0, stream, pool,
-                       block_table, context_lens, dense, num_kv_heads, head_dim, bs_shift, max_blocks);
+    switch (head_dim) {
+    case 64: launch_split<64, true>(a, stream); break;
+    case 128: launch_split<128, true>(a, stream); break;
+    case 256: launch_split<256, true>(a, stream); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ int32_t rra_varlen_attn_fwd_gqa(const void *q, const void *k, const void *v, voi
     if (!good_scale(softmax_scale)) return RRA_ERR_INVALID_ARG;
     if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
     if (batch == 0 || max_seqlen_q == 0) return RRA_OK;  // no query rows exist
-    if (!q || !out || !lse || !cu_seqlens_q || !cu_seqlens_k) return RRA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k) return RRA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
         return RRA_ERR_INVALID_ARG;
 
@@ -216,6 +216,35 @@ int32_t rra_varlen_attn_bwd(const void *q, const void *k, const void *v, const v
     return hip_status(launch_varlen_bwd(a, causal == 1, device_cus(), static_cast<hipStream_t>(stream)));
 }
 
+static int32_t pack_call(const void *src, void *dst, const int32_t *cu_seqlens, int32_t batch, int32_t max_seqlen,
+                         int64_t row_bytes, bool to_packed, void *stream)
+{
+    if (batch < 0 || max_seqlen < 0 || row_bytes <= 0 || row_bytes % 4 != 0) return RRA_ERR_INVALID_ARG;
+    if (batch == 0 || max_seqlen == 0) return RRA_OK;
+    if (!src || !dst || !cu_seqlens) return RRA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(src) & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u)) return RRA_ERR_INVALID_ARG;
+    // one workgroup per run of rows of one sequence; a row's pieces are
+    // counted in 32 bits
+    const int64_t rows = pack_rows_per_wg(row_bytes);
+    const int64_t wgs = (int64_t)batch * ((max_seqlen + rows - 1) / rows);
+    if (wgs > INT32_MAX || row_bytes / 4 > INT32_MAX) return RRA_ERR_INVALID_ARG;
+    const bool vec16 = row_bytes % 16 == 0 && aligned16(src) && aligned16(dst);
+    return hip_status(launch_pack_rows(src, dst, cu_seqlens, batch, max_seqlen, row_bytes, to_packed, vec16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t rra_pack_rows(const void *padded, void *packed, const int32_t *cu_seqlens, int32_t batch,
+                      int32_t max_seqlen, int64_t row_bytes, void *stream)
+{
+    return pack_call(padded, packed, cu_seqlens, batch, max_seqlen, row_bytes, true, stream);
+}
+
+int32_t rra_unpack_rows(const void *packed, void *padded, const int32_t *cu_seqlens, int32_t batch,
+                        int32_t max_seqlen, int64_t row_bytes, void *stream)
+{
+    return pack_call(packed, padded, cu_seqlens, batch, max_seqlen, row_bytes, false, stream);
+}
+
 int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, int32_t num_heads,
                                   int32_t max_seqlen_q, int32_t head_dim, int32_t *items_out, int64_t capacity,
                                   int64_t *item_count, void *stream)
@@ -245,10 +274,11 @@ size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
 
 // Checks and DecodeArgs set-up shared by the one-shot decode and the
 // stateful step: everything except the context source and the destination.
+// (gather: the test hook, which reads no q and takes no scale.)
 static int32_t decode_setup(DecodeArgs &a, const void *q, const void *k_pool, const void *v_pool,
                             const int32_t *block_table, int32_t num_seqs, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks,
-                            float softmax_scale, void *workspace, size_t workspace_bytes)
+                            float softmax_scale, void *workspace, size_t workspace_bytes, bool gather = false)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         max_blocks < 0)
@@ -261,7 +291,7 @@ static int32_t decode_setup(DecodeArgs &a, const void *q, const void *k_pool, co
     if ((int64_t)max_blocks * block_size > INT32_MAX) return RRA_ERR_INVALID_ARG;
     if ((int64_t)num_seqs * num_q_heads > INT32_MAX) return RRA_ERR_INVALID_ARG;  // one combine workgroup each
     if (num_seqs == 0) return RRA_OK;
-    if (!q || !block_table) return RRA_ERR_INVALID_ARG;
+    if ((!gather && !q) || !k_pool || !v_pool || !block_table) return RRA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return RRA_ERR_INVALID_ARG;
     const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RRA_ERR_WORKSPACE;
@@ -357,23 +387,21 @@ int32_t rra_paged_decode_state_init(float *state_m, float *state_l, float *state
                                                head_dim, static_cast<hipStream_t>(stream)));
 }
 
-int32_t rra_debug_paged_gather(const void *pool, const int32_t *block_table, const int32_t *context_lens,
-                               void *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, int32_t max_blocks_per_seq, void *stream)
+int32_t rra_debug_paged_gather(const void *k_pool, const void *v_pool, const int32_t *block_table,
+                               const int32_t *context_lens, void *k_dense, void *v_dense, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
+    DecodeArgs a;
+    const int32_t rc = decode_setup(a, nullptr, k_pool, v_pool, block_table, num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, block_size, max_blocks_per_seq, 1.f, workspace, workspace_bytes, true);
+    if (rc != RRA_OK || num_seqs == 0) return rc;
+    if (!context_lens || !k_dense || !v_dense || !aligned16(k_dense) || !aligned16(v_dense))
         return RRA_ERR_INVALID_ARG;
-    if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
-    const int32_t bs_shift = log2_exact(block_size);
-    if (bs_shift < 0 || block_size > 1024) return RRA_ERR_UNSUPPORTED;
-    if (num_seqs == 0 || max_blocks_per_seq == 0) return RRA_OK;
-    if (!pool || !block_table || !context_lens || !dense) return RRA_ERR_INVALID_ARG;
-    if (!aligned16(pool) || !aligned16(dense)) return RRA_ERR_INVALID_ARG;
-    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 31) return RRA_ERR_INVALID_ARG;
-    return hip_status(launch_paged_gather(static_cast<const uint16_t *>(pool), block_table, context_lens,
-                                          static_cast<uint16_t *>(dense), num_seqs, num_kv_heads, head_dim,
-                                          block_size, bs_shift, max_blocks_per_seq,
-                                          static_cast<hipStream_t>(stream)));
+    a.context_lens = context_lens;
+    a.gather_k = static_cast<uint16_t *>(k_dense);
+    a.gather_v = static_cast<uint16_t *>(v_dense);
+    return hip_status(launch_paged_gather(a, head_dim, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -80,6 +80,7 @@ struct DecodeArgs {
     const int32_t *block_counts, *token_counts;  // stateful step (context_lens null)
     float *st_m, *st_l, *st_o;  // stateful step: the caller's state, merged in place
     uint16_t *out;
+    uint16_t *gather_k, *gather_v;  // test hook only: dense copies of the loaded K and V rows
     int32_t *ws_goff;    // [num_seqs + 1] token-group offsets of the sequences
     float *ws_m, *ws_l, *ws_o;  // [n_ranges + num_seqs] x num_q_heads partial states
     int32_t num_seqs, num_q_heads, num_kv_heads;
@@ -97,8 +98,14 @@ hipError_t launch_decode_finalize(const float *state_l, const float *state_o, ui
                                   int32_t head_dim, hipStream_t stream);
 hipError_t launch_decode_state_init(float *state_m, float *state_l, float *state_o, int64_t units, int32_t head_dim,
                                     hipStream_t stream);
-hipError_t launch_paged_gather(const uint16_t *pool, const int32_t *block_table, const int32_t *context_lens,
-                               uint16_t *dense, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, int32_t bs_shift, int32_t max_blocks, hipStream_t stream);
+// The decode split kernel in its gather mode (test hook): a.gather_k and
+// a.gather_v receive the K and V rows its loads fetch.
+hipError_t launch_paged_gather(const DecodeArgs &a, int head_dim, hipStream_t stream);
+
+// Padded <-> packed row copies (pack_rows.hip).  Rows of one workgroup:
+// about 16 KiB worth.
+int64_t pack_rows_per_wg(int64_t row_bytes);
+hipError_t launch_pack_rows(const void *src, void *dst, const int32_t *cu, int32_t batch, int32_t max_seqlen,
+                            int64_t row_bytes, bool to_packed, bool vec16, hipStream_t stream);
 
 }  // namespace rra
