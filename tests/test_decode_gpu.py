@@ -79,6 +79,16 @@ def test_decode_full_config():
     check(c, "paged_decode full")
 
 
+@pytest.mark.parametrize("q_mult", [4.0, 16.0])
+def test_decode_peaked(q_mult):
+    """q scaled by a power of two (exact in bf16): peaked softmax rows whose
+    running max moves many times, where a dominant weight must not carry its
+    bf16 rounding into the output."""
+    c = I.decode_case("peaked", [1, 300, 4097, 64, 2000], 8, 2, 128, 16, seed=333)
+    c.q = I.bf16_bits(I.bf16_to_f32(c.q) * np.float32(q_mult))
+    check(c, f"peaked q x{q_mult:g}")
+
+
 def test_decode_deterministic():
     c = I.decode_case("det", [4000, 17, 900], 32, 8, 128, 16, seed=9)
     assert np.array_equal(run_decode(c), run_decode(c))

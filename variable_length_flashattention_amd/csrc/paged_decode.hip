@@ -25,8 +25,10 @@
 // Per 16 tokens a wave computes
 //   S^T[token][q head] = K . Q^T     (v_mfma_f32_16x16x32_bf16; K straight
 //                                     from the pool into the A operand)
-//   the online softmax per q head (cross-lane max only when a score exceeds
-//   the running reference max by more than 2^8 in probability),
+//   the online softmax per q head (the cross-lane max and the rescale of o
+//   and l only when a score exceeds the running max, so every probability
+//   is at most 1 and a dominant one is exactly 1: its bf16 rounding for the
+//   MMA then costs nothing, while l sums the fp32 values),
 //   O^T[d][q head] += V^T . P^T      (v_mfma_f32_16x16x16_bf16; V staged in
 //                                     wave-private LDS, read transposed).
 // Only tokens t < ctx (the sequence's clamped token count) are read; the
@@ -203,7 +205,6 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
     const int Hkv = a.num_kv_heads;
     const int bs_shift = a.bs_shift;
     const float sl2 = a.scale_log2;
-    const float thresh = 8.f / sl2;                // raw-score headroom above the reference max
     const int64_t row_elems = (int64_t)Hkv * D;    // elements per pool token row
 
     for (int s = go.seq_of_group(g_lo, lane), gs0 = go.goff(s); s < S && gs0 < g_hi; s++) {
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeArgs a)
                 for (int r = 0; r < 4; r++)
                     if (t0 + 4 * grp + r >= t_end) sv[r] = -INFINITY;
                 const float lmax = max3f(sv[0], sv[1], max3f(sv[2], sv[3], sv[3]));
-                if (__builtin_amdgcn_ballot_w64(lmax > m_ref + thresh || (m_ref == -INFINITY && lmax > -INFINITY))) {
+                if (__builtin_amdgcn_ballot_w64(lmax > m_ref)) {
                     float mx = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
                     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
                     const float m_new = fmaxf(m_ref, mx);

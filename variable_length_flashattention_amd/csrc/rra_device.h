@@ -37,6 +37,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     b2 r = __builtin_convertvector(v, b2);
     return __builtin_bit_cast(uint32_t, r);
 }
+// lo + hi of a packed bf16 pair, added to acc in fp32 (one v_dot2_f32_bf16
+// against (1, 1); the products are exact).
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, pair), __builtin_bit_cast(b2, 0x3F803F80u), acc,
+                                           false);
+}
 // The two floats a packed bf16 pair represents.
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }

@@ -15,8 +15,11 @@
 // double-buffered so that loads run ahead of the compute.  Per key tile each wave
 //   S^T[key][query] = K . Q^T          (v_mfma_f32_32x32x16_bf16, Q in VGPRs)
 //   masks the tail and the causal diagonal (bottom-right: j <= i + Lk - Lq),
-//   updates m and l (exp2 with log2(e) folded into the scale; l sums the fp32
-//   probabilities, the MMA takes them rounded to bf16),
+//   updates m and l (exp2 with log2(e) folded into the scale; the MMA takes
+//   the probabilities rounded to bf16, and the row sums are kept twice: of
+//   the fp32 probabilities for lse, and of the bf16 values the MMA takes for
+//   the normalisation of out, so that out is an exact convex combination of
+//   the rows of V with the weights the MMA used),
 //   O^T[d][query] += V^T . P^T         (V^T read with ds_read_b64_tr_b16).
 // The S^T orientation puts one query per lane column, so row statistics are
 // lane-local plus one permlane32 swap, and P^T feeds the second MMA straight
@@ -244,12 +247,14 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         // m_ref: the max the accumulators are currently scaled to; it is only
         // raised when a tile's probabilities against it grow too large (a
         // lane's share of a row sum above 2^15), which skips most row-max
-        // reductions and rescales of O.
-        float m_ref[RPW], l_run[RPW];
+        // reductions and rescales of O.  l_run sums the fp32 probabilities
+        // (for lse), l_mma the bf16 values the PV MMA takes (for out).
+        float m_ref[RPW], l_run[RPW], l_mma[RPW];
 #pragma unroll
         for (int u = 0; u < RPW; u++) {
             m_ref[u] = -INFINITY;
             l_run[u] = 0.f;
+            l_mma[u] = 0.f;
         }
 
         // one key tile; tile kt lives in buffer kt % 2, and tile kt+1 is
@@ -331,10 +336,16 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                 // exact max (and rescales O and l) when a row has no reference
                 // yet or this lane's share of the row sum exceeds 2^15 (every
                 // probability then stays <= 2^15, far inside fp32/bf16 range).
-                // l sums the fp32 probabilities (summing their bf16 roundings
-                // would cost lse up to ~2^-9 on rows with few keys).
+                // l_run sums the fp32 probabilities (summing their bf16
+                // roundings would cost lse up to ~2^-9 on rows with few keys);
+                // l_mma sums the bf16 values, so that out = O / l_mma weighs
+                // each V row by exactly what the MMA used (with the fp32 sum a
+                // dominant weight above 1 would be off by its rounding, up to
+                // 2^-9 |v|).
+                float rb = 0.f;
                 auto probs = [&](float mc) __attribute__((always_inline)) -> float {
                     float rs = 0.f;
+                    rb = 0.f;
 #pragma unroll
                     for (int c = 0; c < NC; c++)
 #pragma unroll
@@ -343,6 +354,7 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                             const float p1 = fast_exp2(fmaf(s[u][c][2 * r2 + 1], sl2, -mc));
                             pk[u][c][r2] = pack_bf16x2(p0, p1);
                             rs += p0 + p1;
+                            rb = add_bf16x2(pk[u][c][r2], rb);
                         }
                     return rs;
                 };
@@ -363,6 +375,7 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                     const float alpha =
                         (m_ref[u] == -INFINITY || m_new == m_ref[u]) ? 1.f : fast_exp2((m_ref[u] - m_new) * sl2);
                     l_run[u] *= alpha;
+                    l_mma[u] *= alpha;
 #pragma unroll
                     for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
@@ -371,6 +384,7 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                     rs = probs((m_new == -INFINITY ? 0.f : m_new) * sl2);
                 }
                 l_run[u] += sum_across_halves(rs);
+                l_mma[u] += sum_across_halves(rb);
             }
 
             // O^T += V^T P^T, 16 keys per MMA; each V operand read feeds every
@@ -414,11 +428,11 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
 
-        // epilogue: out = O / l (0 when no key is visible), lse = scale*m + ln l (-inf then)
+        // epilogue: out = O / l_mma (0 when no key is visible), lse = scale*m + ln l_run (-inf then)
 #pragma unroll
         for (int u = 0; u < RPW; u++) {
             if (!row_ok[u]) continue;
-            const float inv_l = l_run[u] > 0.f ? 1.f / l_run[u] : 0.f;
+            const float inv_l = l_run[u] > 0.f ? 1.f / l_mma[u] : 0.f;
             uint16_t *orow = a.out + ((int64_t)(q0 + my_i[u]) * H + h) * D + 4 * (lane >> 5);
 #pragma unroll
             for (int dc = 0; dc < NDC; dc++)
