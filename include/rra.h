@@ -38,6 +38,7 @@ extern "C" {
 #define RRA_ERR_UNSUPPORTED    2  /* valid but not implemented (e.g. head_dim not 64/128/256) */
 #define RRA_ERR_WORKSPACE      3  /* decode workspace missing or too small */
 #define RRA_ERR_HIP            4  /* the HIP runtime reported an error at launch */
+#define RRA_ERR_SCRATCH        5  /* the sizes need more than the library's static decode scratch */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *rra_status_string(int32_t status);
@@ -201,6 +202,32 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
  * sequence) piece bound plus the sequences' token-group offsets. */
 size_t rra_paged_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim);
+
+/*
+ * Allocation-free variant of rra_paged_decode_attn, for callers that cannot
+ * allocate device memory or hand over a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, layouts and result as rra_paged_decode_attn, without the
+ * workspace: the partial softmax states live in a static device array that
+ * the library holds on each GPU it runs on, for the life of the process
+ * (rra_paged_decode_scratch_bytes() bytes, 32 MiB; the call allocates
+ * nothing, and the array's contents on entry do not matter).  Sizes whose
+ * workspace (rra_paged_decode_workspace_bytes) exceeds it are rejected with
+ * RRA_ERR_SCRATCH before any HIP call; e.g. 32 q heads over 8 kv heads fit
+ * up to 1760 sequences at head_dim 128 (887 at 256, 3458 at 64).  All calls
+ * on one GPU share the array: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and give wrong results;
+ * calls ordered on one stream are safe.  The first call on a device looks
+ * up that device's copy (hipGetSymbolAddress) with the device current.
+ */
+int32_t rra_paged_decode_attn_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                      const int32_t *block_table, const int32_t *context_lens, void *out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                      float softmax_scale, void *stream);
+
+/* Bytes of the static scratch rra_paged_decode_attn_noalloc uses per GPU. */
+size_t rra_paged_decode_scratch_bytes(void);
 
 /*
  * Stateful decode ([DECODE] AttnState, step_tile_ref, finalize_ref): the

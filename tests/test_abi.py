@@ -256,3 +256,25 @@ def test_debug_tile_map_validation(lib):
 ])
 def test_pack_rows_validation(lib, fn, args, status):
     assert getattr(lib, fn)(*args, None) == status
+
+
+def test_noalloc_decode_validation(lib):
+    """The allocation-free decode validates before any HIP call: sizes whose
+    partial states exceed the static scratch return RRA_ERR_SCRATCH; bad
+    arguments return the statuses of rra_paged_decode_attn."""
+    lim = rra.rra_paged_decode_scratch_bytes()
+    assert lim == 32 << 20
+    big = 1
+    while rra.rra_paged_decode_workspace_bytes(big, 32, 8, 128) <= lim:
+        big += 64
+    def st(**kw):
+        a = dict(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, out=FAKE, S=4, Hq=32, Hkv=8, D=128, BS=16, MB=8,
+                 scale=0.1)
+        a.update(kw)
+        return lib.rra_paged_decode_attn_noalloc(a["q"], a["kp"], a["vp"], a["bt"], a["cl"], a["out"], a["S"],
+                                                 a["Hq"], a["Hkv"], a["D"], a["BS"], a["MB"], a["scale"], None)
+    assert st(S=big) == 5 and rra.rra_status_string(5) == "RRA_ERR_SCRATCH"
+    assert st(S=-1) == 1 and st(Hq=12) == 1 and st(scale=0.0) == 1 and st(D=80) == 2 and st(BS=12) == 2
+    assert st(q=None) == 1 and st(kp=None) == 1 and st(out=None) == 1 and st(cl=None) == 1 and st(bt=None) == 1
+    assert st(out=FAKE + 2) == 1
+    assert st(S=0) == 0 and st(S=0, q=None) == 0

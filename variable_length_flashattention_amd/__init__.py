@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     rra_varlen_block_q,
     rra_paged_decode_attn,
     rra_paged_decode_workspace_bytes,
+    rra_paged_decode_attn_noalloc,
+    rra_paged_decode_scratch_bytes,
     rra_paged_decode_state_init,
     rra_paged_decode_step,
     rra_paged_decode_finalize,

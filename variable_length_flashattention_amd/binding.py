@@ -23,6 +23,7 @@ RRA_ERR_INVALID_ARG = 1
 RRA_ERR_UNSUPPORTED = 2
 RRA_ERR_WORKSPACE = 3
 RRA_ERR_HIP = 4
+RRA_ERR_SCRATCH = 5
 
 
 class RraError(RuntimeError):
@@ -65,6 +66,10 @@ def load_library():
     lib.rra_varlen_block_q.restype = i32
     lib.rra_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.rra_paged_decode_attn.restype = i32
+    lib.rra_paged_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.rra_paged_decode_attn_noalloc.restype = i32
+    lib.rra_paged_decode_scratch_bytes.argtypes = []
+    lib.rra_paged_decode_scratch_bytes.restype = sz
     lib.rra_paged_decode_state_init.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.rra_paged_decode_state_init.restype = i32
     lib.rra_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp,
@@ -173,6 +178,19 @@ def rra_paged_decode_attn(q, k_pool, v_pool, block_table, context_lens, out, num
         float(softmax_scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("rra_paged_decode_attn", st)
 
+
+def rra_paged_decode_attn_noalloc(q, k_pool, v_pool, block_table, context_lens, out, num_seqs, num_q_heads,
+                                  num_kv_heads, head_dim, block_size, max_blocks_per_seq, softmax_scale,
+                                  stream=None):
+    st = load_library().rra_paged_decode_attn_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens), _ptr(out), int(num_seqs),
+        int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size), int(max_blocks_per_seq),
+        float(softmax_scale), _stream(stream))
+    _check("rra_paged_decode_attn_noalloc", st)
+
+
+def rra_paged_decode_scratch_bytes() -> int:
+    return int(load_library().rra_paged_decode_scratch_bytes())
 
 def rra_paged_decode_state_init(state_m, state_l, state_o, num_seqs, num_q_heads, head_dim, stream=None):
     st = load_library().rra_paged_decode_state_init(_ptr(state_m), _ptr(state_l), _ptr(state_o), int(num_seqs),

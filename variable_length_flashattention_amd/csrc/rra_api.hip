@@ -3,6 +3,7 @@
 // launch nothing.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/rra.h"
 #include "rra_internal.h"
@@ -41,6 +42,31 @@ int device_cus()
     return cached[dev];
 }
 
+// Scratch of rra_paged_decode_attn_noalloc: the decode workspace (token-group
+// offsets and fp32 partial states) of one call, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy of the array
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels get the address scratch_ptr() looked up.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+// This device's copy of `scratch` (looked up once per device, with the
+// device current).  nullptr on a HIP error.
+void *scratch_ptr()
+{
+    static std::mutex mu;
+    static void *ptrs[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,6 +79,7 @@ const char *rra_status_string(int32_t status)
     case RRA_ERR_UNSUPPORTED: return "RRA_ERR_UNSUPPORTED";
     case RRA_ERR_WORKSPACE: return "RRA_ERR_WORKSPACE";
     case RRA_ERR_HIP: return "RRA_ERR_HIP";
+    case RRA_ERR_SCRATCH: return "RRA_ERR_SCRATCH";
     default: return "RRA_UNKNOWN_STATUS";
     }
 }
@@ -339,6 +366,33 @@ int32_t rra_paged_decode_attn(const void *q, const void *k_pool, const void *v_p
                                     workspace_bytes);
     if (rc != RRA_OK || num_seqs == 0) return rc;
     if (!context_lens || !out || !aligned16(out)) return RRA_ERR_INVALID_ARG;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint16_t *>(out);
+    return hip_status(launch_paged_decode(a, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+size_t rra_paged_decode_scratch_bytes(void) { return kDecodeScratchBytes; }
+
+int32_t rra_paged_decode_attn_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                      const int32_t *block_table, const int32_t *context_lens, void *out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, float softmax_scale,
+                                      void *stream)
+{
+    // Validate first, with a stand-in address for the scratch (decode_setup
+    // only checks its alignment): a rejected call makes no HIP call.
+    DecodeArgs a;
+    void *const stand_in = reinterpret_cast<void *>((uintptr_t)256);
+    int32_t rc = decode_setup(a, q, k_pool, v_pool, block_table, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              block_size, max_blocks_per_seq, softmax_scale, stand_in, kDecodeScratchBytes);
+    if (rc == RRA_ERR_WORKSPACE) return RRA_ERR_SCRATCH;  // the partial states need more than the scratch holds
+    if (rc != RRA_OK || num_seqs == 0) return rc;
+    if (!context_lens || !out || !aligned16(out)) return RRA_ERR_INVALID_ARG;
+    void *ws = scratch_ptr();
+    if (!ws) return RRA_ERR_HIP;
+    rc = decode_setup(a, q, k_pool, v_pool, block_table, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, softmax_scale, ws, kDecodeScratchBytes);
+    if (rc != RRA_OK) return rc;
     a.context_lens = context_lens;
     a.out = static_cast<uint16_t *>(out);
     return hip_status(launch_paged_decode(a, head_dim, static_cast<hipStream_t>(stream)));
