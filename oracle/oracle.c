@@ -502,59 +502,84 @@ static void decode_direct_unit(void *p, int64_t unit, double *scratch)
     }
 }
 
-/* One token of the decode page's recurrence (step_tile_ref): score x, value
- * row vr; the state (m, l, o) moves to the new running max. */
-static void fold_token(double *m, double *l, double *o, double x, const uint16_t *vr, int64_t D)
+/* Merge a tile's own softmax state (t_max, t_den, t_acc) into a running
+ * state (run_max, run_den, run_acc): both are rescaled to the larger of the
+ * two maxima (an empty state, max = -inf, gets weight 0). */
+static void merge_state(double *run_max, double *run_den, double *run_acc, double t_max, double t_den,
+                        const double *t_acc, int64_t D)
 {
-    const double m_new = x > *m ? x : *m;
-    const double scale_old = exp(*m - m_new);
-    const double scale_new = exp(x - m_new);
-    *l = *l * scale_old + scale_new;
-    for (int64_t d = 0; d < D; d++) o[d] = o[d] * scale_old + scale_new * bf16_value(vr[d]);
-    *m = m_new;
+    const double top = t_max > *run_max ? t_max : *run_max;
+    if (top == -INFINITY) return; /* both empty */
+    const double w_run = *run_max == -INFINITY ? 0.0 : exp(*run_max - top);
+    const double w_tile = t_max == -INFINITY ? 0.0 : exp(t_max - top);
+    *run_den = *run_den * w_run + t_den * w_tile;
+    for (int64_t d = 0; d < D; d++) run_acc[d] = run_acc[d] * w_run + t_acc[d] * w_tile;
+    *run_max = top;
 }
 
-/* The decode page's route: running state (m, l, o) starting at (-inf, 0, 0),
- * one token at a time in block-table order:
- *   m' = max(m, x);  l = l*exp(m - m') + exp(x - m');  o = o*exp(m - m') + exp(x - m')*v;  m = m'
- * with the state stored and reloaded between tiles of tile_capacity blocks
- * (AttnState carried across step_tile_ref calls), then finalize:
- * out = o / l if l > 0 else 0 (finalize_ref). */
+/* The softmax state of one tile of tokens, from its definition: scores[i]
+ * of the n tokens (already scaled), their maximum, then the sum of
+ * exp(score - max) and the same weights applied to the V rows (vrow(i) =
+ * pool + voff[i]).  t_acc receives D doubles. */
+static void tile_state(const double *scores, const int64_t *voff, const uint16_t *pool, int64_t n, int64_t D,
+                       double *t_max, double *t_den, double *t_acc)
+{
+    double mx = -INFINITY;
+    for (int64_t i = 0; i < n; i++)
+        if (scores[i] > mx) mx = scores[i];
+    *t_max = mx;
+    *t_den = 0.0;
+    for (int64_t d = 0; d < D; d++) t_acc[d] = 0.0;
+    if (mx == -INFINITY) return;
+    for (int64_t i = 0; i < n; i++) {
+        const double w = exp(scores[i] - mx);
+        *t_den += w;
+        for (int64_t d = 0; d < D; d++) t_acc[d] += w * bf16_value(pool[voff[i] + d]);
+    }
+}
+
+/* Score of q row qrow against the pool row at koff (scaled). */
+static double pool_score(const uint16_t *qrow, const uint16_t *k_pool, int64_t koff, int64_t D, double scale)
+{
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(k_pool[koff + d]);
+    return scale * dot;
+}
+
+/* The decode page's route (AttnState carried across step_tile_ref calls,
+ * then finalize_ref): the context is visited in tiles of tile_capacity
+ * blocks in block-table order; each tile's own state is merged into the
+ * running state (-inf, 0, 0 at the start), which is all that is kept from
+ * one tile to the next; then out = o / l if l > 0 else 0.  scratch holds
+ * D + 2 * tile_capacity * BS doubles. */
 static void decode_recurrent_unit(void *p, int64_t unit, double *scratch)
 {
-    (void)scratch;
     const decode_ctx *c = (const decode_ctx *)p;
     const int32_t s = (int32_t)(unit / c->Hq), qh = (int32_t)(unit % c->Hq);
     const int32_t kh = qh / (c->Hq / c->Hkv);
     const int64_t ctx = c->context_lens[s], D = c->D;
     const uint16_t *qrow = c->q + ((int64_t)s * c->Hq + qh) * D;
     double *o_out = c->out + ((int64_t)s * c->Hq + qh) * D;
+    const int64_t cap_tok = (int64_t)c->tile_capacity * c->BS;
+    double *t_acc = scratch, *scores = scratch + D;
+    int64_t *voff = (int64_t *)(scratch + D + cap_tok);
 
-    /* carried state, as kept between tile calls */
-    double st_m = -INFINITY, st_l = 0.0;
-    double *st_o = scratch; /* D doubles */
-    for (int64_t d = 0; d < D; d++) st_o[d] = 0.0;
-
-    const int64_t n_blocks = (ctx + c->BS - 1) / c->BS;
-    for (int64_t tile0 = 0; tile0 < n_blocks; tile0 += c->tile_capacity) {
-        double m = st_m, l = st_l; /* load state */
-        double *o = st_o;
-        const int64_t tile1 = tile0 + c->tile_capacity < n_blocks ? tile0 + c->tile_capacity : n_blocks;
-        for (int64_t blk = tile0; blk < tile1; blk++) {
-            for (int64_t slot = 0; slot < c->BS; slot++) {
-                const int64_t t = blk * c->BS + slot;
-                if (t >= ctx) break;
-                const uint16_t *kr = pool_row(c, c->k_pool, s, t, kh);
-                const uint16_t *vr = pool_row(c, c->v_pool, s, t, kh);
-                double dot = 0.0;
-                for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(kr[d]);
-                fold_token(&m, &l, o, c->scale * dot, vr, D);
-            }
+    double run_max = -INFINITY, run_den = 0.0;
+    double *run_acc = o_out; /* the running numerator lives in the output row */
+    for (int64_t d = 0; d < D; d++) run_acc[d] = 0.0;
+    for (int64_t first = 0; first < ctx; first += cap_tok) {
+        const int64_t n = ctx - first < cap_tok ? ctx - first : cap_tok;
+        for (int64_t i = 0; i < n; i++) {
+            const int64_t koff = pool_row(c, c->k_pool, s, first + i, kh) - c->k_pool;
+            scores[i] = pool_score(qrow, c->k_pool, koff, D, c->scale);
+            voff[i] = pool_row(c, c->v_pool, s, first + i, kh) - c->v_pool;
         }
-        st_m = m; st_l = l; /* store state */
+        double t_max, t_den;
+        tile_state(scores, voff, c->v_pool, n, D, &t_max, &t_den, t_acc);
+        merge_state(&run_max, &run_den, run_acc, t_max, t_den, t_acc, D);
     }
-    const double inv_l = st_l > 0.0 ? 1.0 / st_l : 0.0;
-    for (int64_t d = 0; d < D; d++) o_out[d] = st_o[d] * inv_l;
+    const double inv_l = run_den > 0.0 ? 1.0 / run_den : 0.0;
+    for (int64_t d = 0; d < D; d++) o_out[d] *= inv_l;
 }
 
 static int decode_check(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
@@ -599,16 +624,22 @@ int oracle_paged_decode_recurrent(const uint16_t *q, const uint16_t *k_pool, con
     if (tile_capacity <= 0) return -1;
     decode_ctx c = {q, k_pool, v_pool, block_table, context_lens, num_seqs, num_q_heads, num_kv_heads,
                     head_dim, block_size, max_blocks_per_seq, scale, tile_capacity, out};
-    return run_units(decode_recurrent_unit, &c, (int64_t)num_seqs * num_q_heads, (size_t)head_dim, nthreads);
+    const size_t cap_tok = (size_t)tile_capacity * (size_t)block_size;
+    return run_units(decode_recurrent_unit, &c, (int64_t)num_seqs * num_q_heads, (size_t)head_dim + 2 * cap_tok,
+                     nthreads);
 }
 
 /* The decode page's stateful interface.  The caller owns the state
- * (AttnState): m, l [S, Hq] and o [S, Hq, D], starting at (-inf, 0, 0).  A
- * step (step_tile_ref) folds, for every sequence s, the tokens of the blocks
- * tile_blocks[s, 0 .. tile_block_counts[s]) in order, every token of each
- * block unless token_counts is given, in which case the tile ends after
- * token_counts[s] tokens (a partly filled last block).  finalize_ref turns
- * the state into out = o / l (0 where l == 0). */
+ * (AttnState): m, l [S, Hq] and o [S, Hq, D], starting at (-inf, 0, 0): the
+ * largest scaled score seen, the sum of exp(score - m) and the same weights
+ * applied to the V rows.  A step (step_tile_ref) takes, for every sequence
+ * s, the tokens of the blocks tile_blocks[s, 0 .. tile_block_counts[s]) in
+ * order, every token of each block unless token_counts is given, in which
+ * case the tile ends after token_counts[s] tokens (a partly filled last
+ * block); the state afterwards is that of the old tokens and the tile's
+ * together, formed here as the tile's own state merged into the carried one
+ * (tile_state, merge_state).  finalize_ref turns the state into out = o / l
+ * (0 where l == 0).  scratch: D + 2 * tile_capacity * BS + 1 doubles. */
 typedef struct {
     double *m, *l, *o;
     const uint16_t *q, *k_pool, *v_pool;
@@ -619,28 +650,33 @@ typedef struct {
 
 static void decode_step_unit(void *p, int64_t unit, double *scratch)
 {
-    (void)scratch;
     const step_ctx *c = (const step_ctx *)p;
     const int32_t s = (int32_t)(unit / c->Hq), qh = (int32_t)(unit % c->Hq);
     const int32_t kh = qh / (c->Hq / c->Hkv);
     const int64_t D = c->D;
     const uint16_t *qrow = c->q + ((int64_t)s * c->Hq + qh) * D;
-    double m = c->m[unit], l = c->l[unit];
-    double *o = c->o + unit * D;
+    const int64_t cap_tok = (int64_t)c->tile_capacity * c->BS;
+    double *t_acc = scratch, *scores = scratch + D;
+    int64_t *voff = (int64_t *)(scratch + D + cap_tok);
+    /* the tile's tokens: the first n_tok slots of its listed blocks, in order */
     const int64_t n_tok = c->token_counts ? c->token_counts[s] : (int64_t)c->tile_block_counts[s] * c->BS;
+    int64_t n = 0;
     for (int64_t b = 0; b < c->tile_block_counts[s]; b++) {
         const int64_t blk = c->tile_blocks[(int64_t)s * c->tile_capacity + b];
         for (int64_t slot = 0; slot < c->BS; slot++) {
             if (b * c->BS + slot >= n_tok) break;
-            const uint16_t *kr = c->k_pool + ((blk * c->BS + slot) * c->Hkv + kh) * D;
-            const uint16_t *vr = c->v_pool + ((blk * c->BS + slot) * c->Hkv + kh) * D;
-            double dot = 0.0;
-            for (int64_t d = 0; d < D; d++) dot += bf16_value(qrow[d]) * bf16_value(kr[d]);
-            fold_token(&m, &l, o, c->scale * dot, vr, D);
+            const int64_t row = ((blk * c->BS + slot) * c->Hkv + kh) * D;
+            scores[n] = pool_score(qrow, c->k_pool, row, D, c->scale);
+            voff[n++] = row;
         }
     }
-    c->m[unit] = m;
-    c->l[unit] = l;
+    double t_max, t_den;
+    tile_state(scores, voff, c->v_pool, n, D, &t_max, &t_den, t_acc);
+    /* the caller's state, carried in from the previous step */
+    double carried_max = c->m[unit], carried_den = c->l[unit];
+    merge_state(&carried_max, &carried_den, c->o + unit * D, t_max, t_den, t_acc, D);
+    c->m[unit] = carried_max;
+    c->l[unit] = carried_den;
 }
 
 int oracle_paged_decode_step(double *state_m, double *state_l, double *state_o,
@@ -659,7 +695,9 @@ int oracle_paged_decode_step(double *state_m, double *state_l, double *state_o,
     }
     step_ctx c = {state_m, state_l, state_o, q, k_pool, v_pool, tile_blocks, tile_block_counts, token_counts,
                   num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, tile_capacity, scale};
-    return run_units(decode_step_unit, &c, (int64_t)num_seqs * num_q_heads, 1, nthreads);
+    const size_t cap_tok = (size_t)tile_capacity * (size_t)block_size;
+    return run_units(decode_step_unit, &c, (int64_t)num_seqs * num_q_heads, (size_t)head_dim + 2 * cap_tok + 1,
+                     nthreads);
 }
 
 int oracle_paged_decode_finalize(const double *state_l, const double *state_o, int32_t num_seqs,

@@ -40,12 +40,16 @@ MUTANTS = [
     ("decode_reads_whole_last_block", "for (int64_t t = 0; t < ctx; t++) {\n        const uint16_t *kr",
      "for (int64_t t = 0; t < (ctx + c->BS - 1) / c->BS * c->BS; t++) {\n        const uint16_t *kr"),
     ("decode_slot_from_block", "const int64_t slot = t % c->BS;", "const int64_t slot = t / c->BS % c->BS;"),
-    ("recurrence_rescale_sign", "const double scale_old = exp(*m - m_new);", "const double scale_old = exp(m_new - *m);"),
+    ("merge_rescale_sign", "const double w_run = *run_max == -INFINITY ? 0.0 : exp(*run_max - top);",
+     "const double w_run = *run_max == -INFINITY ? 0.0 : exp(top - *run_max);"),
+    ("tile_state_max_not_subtracted", "const double w = exp(scores[i] - mx);", "const double w = exp(scores[i]);"),
     ("step_ignores_token_count", "if (b * c->BS + slot >= n_tok) break;", "if (b * c->BS + slot >= c->BS * c->tile_block_counts[s]) break;"),
     ("step_finalize_unguarded", "const double inv_l = state_l[u] > 0.0 ? 1.0 / state_l[u] : 0.0;",
      "const double inv_l = 1.0 / state_l[u];"),
-    ("step_state_not_carried", "double m = c->m[unit], l = c->l[unit];", "double m = -INFINITY, l = 0.0;"),
-    ("finalize_unguarded", "const double inv_l = st_l > 0.0 ? 1.0 / st_l : 0.0;", "const double inv_l = 1.0 / st_l;"),
+    ("step_state_not_carried", "double carried_max = c->m[unit], carried_den = c->l[unit];",
+     "double carried_max = -INFINITY, carried_den = 0.0;"),
+    ("finalize_unguarded", "const double inv_l = run_den > 0.0 ? 1.0 / run_den : 0.0;",
+     "const double inv_l = 1.0 / run_den;"),
     ("bwd_jacobian_without_rowdot", "const double ds = prob[j] * (dprob[j] - rowdot);",
      "const double ds = prob[j] * dprob[j];"),
     ("bwd_dk_unscaled", "dkrow[d] += c->scale * ds * bf16_value(qrow[d]);", "dkrow[d] += ds * bf16_value(qrow[d]);"),
