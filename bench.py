@@ -69,6 +69,8 @@ def dev_bf16(torch, bits):
 
 
 SETTLE_S = 0.5  # seconds of untimed back-to-back launches before the warm-up steps
+COLD_COPIES = 4  # input copies cycled by the HBM-bound many-short runs (4 x 273 MB > the 256 MiB MALL)
+DECODE_COPIES = 2  # the decode's pools are 1.07 GB each: two copies keep every launch cold
 
 
 def time_launches(torch, fn, steps, warmup, settle_s=SETTLE_S):
@@ -103,24 +105,34 @@ def time_launches(torch, fn, steps, warmup, settle_s=SETTLE_S):
 
 
 class VarlenRun:
-    def __init__(self, torch, case):
+    """rra_varlen_attn_fwd (or _gqa) on a case.  With copies > 1 the inputs
+    and outputs exist that many times at different addresses and each launch
+    uses the next copy, so that no launch finds its inputs in the caches (the
+    256 MiB MALL included) from the launch before: a cold measurement."""
+    def __init__(self, torch, case, copies=1):
         import variable_length_flashattention_amd as rra
         self.rra, self.case = rra, case
-        self.q, self.k, self.v = dev_bf16(torch, case.q), dev_bf16(torch, case.k), dev_bf16(torch, case.v)
+        self.sets = []
+        for _ in range(copies):
+            q, k, v = dev_bf16(torch, case.q), dev_bf16(torch, case.k), dev_bf16(torch, case.v)
+            out = torch.empty_like(q)
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+            self.sets.append((q, k, v, out, lse))
+        self.q, self.k, self.v, self.out, self.lse = self.sets[0]
         self.cu_q = torch.from_numpy(case.cu_q).cuda()
         self.cu_k = torch.from_numpy(case.cu_k).cuda()
-        self.out = torch.empty_like(self.q)
-        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+        self.i = 0
 
     def __call__(self):
         c = self.case
+        q, k, v, out, lse = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
         if c.num_kv_heads == c.num_heads:
-            self.rra.rra_varlen_attn_fwd(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
-                                         c.max_seqlen_q, c.batch, c.num_heads, c.head_dim, c.scale, c.causal)
+            self.rra.rra_varlen_attn_fwd(q, k, v, out, lse, self.cu_q, self.cu_k, c.max_seqlen_q, c.batch,
+                                         c.num_heads, c.head_dim, c.scale, c.causal)
         else:
-            self.rra.rra_varlen_attn_fwd_gqa(self.q, self.k, self.v, self.out, self.lse, self.cu_q, self.cu_k,
-                                             c.max_seqlen_q, c.batch, c.num_heads, c.num_kv_heads, c.head_dim,
-                                             c.scale, c.causal)
+            self.rra.rra_varlen_attn_fwd_gqa(q, k, v, out, lse, self.cu_q, self.cu_k, c.max_seqlen_q, c.batch,
+                                             c.num_heads, c.num_kv_heads, c.head_dim, c.scale, c.causal)
 
 
 class BwdRun:
@@ -175,35 +187,43 @@ class PagedRun:
 
 
 class DecodeRun:
-    def __init__(self, torch, case):
+    """rra_paged_decode_attn on a case; with copies > 1 each launch uses the
+    next copy of q, the pools, out and the workspace (cold, as VarlenRun)."""
+    def __init__(self, torch, case, copies=1):
         import variable_length_flashattention_amd as rra
         self.rra, self.case = rra, case
-        self.q = dev_bf16(torch, case.q)
-        self.kp, self.vp = dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)
         self.bt = torch.from_numpy(case.block_table).cuda()
         self.cl = torch.from_numpy(case.context_lens).cuda()
-        self.out = torch.empty_like(self.q)
         need = rra.rra_paged_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                                     case.head_dim)
-        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        self.sets = []
+        for _ in range(copies):
+            q = dev_bf16(torch, case.q)
+            kp, vp = dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            self.sets.append((q, kp, vp, torch.empty_like(q), ws))
+        self.i = 0
 
     def __call__(self):
         c = self.case
-        self.rra.rra_paged_decode_attn(self.q, self.kp, self.vp, self.bt, self.cl, self.out, c.num_seqs,
-                                       c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks,
-                                       c.scale, self.ws, self.ws.numel())
+        q, kp, vp, out, ws = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
+        self.rra.rra_paged_decode_attn(q, kp, vp, self.bt, self.cl, out, c.num_seqs, c.num_q_heads,
+                                       c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks, c.scale, ws,
+                                       ws.numel())
 
 
 class DecodeStepsRun:
     """The stateful decode on the decode workload: state init, the context of
     every sequence folded in n_tiles consecutive tiles of blocks (one
     rra_paged_decode_step each), then finalize."""
-    def __init__(self, torch, case, n_tiles=4):
+    def __init__(self, torch, case, n_tiles=4, copies=1):
         import variable_length_flashattention_amd as rra
         self.rra, self.case = rra, case
         S, BS = case.num_seqs, case.block_size
         self.q = dev_bf16(torch, case.q)
-        self.kp, self.vp = dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)
+        self.pools = [(dev_bf16(torch, case.k_pool), dev_bf16(torch, case.v_pool)) for _ in range(copies)]
+        self.ip = 0
         nblk = (case.context_lens.astype(np.int64) + BS - 1) // BS
         cut = [np.minimum(nblk, (nblk * j + n_tiles - 1) // n_tiles) for j in range(n_tiles + 1)]
         self.cap = max(1, max(int((cut[j + 1] - cut[j]).max()) for j in range(n_tiles)))
@@ -226,9 +246,11 @@ class DecodeStepsRun:
     def __call__(self):
         c, r = self.case, self.rra
         S, Hq, D = c.num_seqs, c.num_q_heads, c.head_dim
+        kp, vp = self.pools[self.ip]
+        self.ip = (self.ip + 1) % len(self.pools)
         r.rra_paged_decode_state_init(self.m, self.l, self.o, S, Hq, D)
         for tb, cnt, tok in self.tiles:
-            r.rra_paged_decode_step(self.m, self.l, self.o, self.q, self.kp, self.vp, tb, cnt, tok, S, Hq,
+            r.rra_paged_decode_step(self.m, self.l, self.o, self.q, kp, vp, tb, cnt, tok, S, Hq,
                                     c.num_kv_heads, D, c.block_size, self.cap, c.scale, self.ws, self.ws.numel())
         r.rra_paged_decode_finalize(self.l, self.o, self.out, S, Hq, D)
 
@@ -300,10 +322,11 @@ def main():
             nbytes, flops = I.varlen_bytes(case.dense), I.varlen_flops(case.dense)
         elif case is None:
             case = I.paged_decode()
-            r = DecodeRun(torch, case)
+            r = DecodeRun(torch, case, copies=DECODE_COPIES)
             nbytes, flops = I.decode_bytes(case), I.decode_flops(case)
         else:
-            r = VarlenRun(torch, case)
+            hbm_bound = args.only.startswith("many_short")
+            r = VarlenRun(torch, case, copies=COLD_COPIES if hbm_bound else 1)
             nbytes, flops = I.varlen_bytes(case), I.varlen_flops(case)
         _, t = time_launches(torch, r, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "avg_us": round(t * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 2),
@@ -352,7 +375,7 @@ def main():
 
     # paged decode (second row of the metric)
     dec = I.paged_decode()
-    drun = DecodeRun(torch, dec)
+    drun = DecodeRun(torch, dec, copies=DECODE_COPIES)
     _, d_avg = time_launches(torch, drun, args.steps, args.warmup)
     dbytes = I.decode_bytes(dec)
     lines["decode"] = {"workload": "paged GQA decode: 64 seqs, ctx U[1,8192] (seed 5001), Hq=32, Hkv=8, "
@@ -361,13 +384,16 @@ def main():
                        "avg_call_us": round(d_avg * 1e6, 2), "bytes_per_call": dbytes,
                        "traffic": load_traffic("paged_decode", kernel_source_hash(DECODE_SOURCES)),
                        "context_tokens": int(dec.context_lens.sum()),
-                       "note": "range-split + combine kernels per call (an offsets kernel too above 256 sequences); working set exceeds the 256 MiB MALL"}
+                       "cold": True, "copies": DECODE_COPIES,
+                       "note": "range-split + combine kernels per call (an offsets kernel too above 256 sequences); "
+                               "consecutive launches use different copies of q and the pools (cold)"}
     del drun
-    srun = DecodeStepsRun(torch, dec)
+    srun = DecodeStepsRun(torch, dec, copies=DECODE_COPIES)
     _, s_avg = time_launches(torch, srun, args.steps, args.warmup)
     lines["decode"]["stateful_4_steps"] = {
         "GB/s": round(dbytes / s_avg / 1e9, 1), "frac_of_hbm_peak": round(dbytes / s_avg / 1e9 / PEAK_HBM_GBS, 4),
         "avg_us": round(s_avg * 1e6, 2),
+        "cold": True, "copies": DECODE_COPIES,
         "note": "state init + 4 rra_paged_decode_step calls (each context cut into 4 tiles of blocks) + finalize"}
     del srun
     torch.cuda.empty_cache()
@@ -398,15 +424,24 @@ def main():
             ("many_short_d256_causal", I.many_short(256, True), "hbm"),
             ("many_short_d256_noncausal", I.many_short(256, False), "hbm"),
         ]:
-            r = PagedRun(torch, case) if isinstance(case, I.PagedPrefillCase) else VarlenRun(torch, case)
+            # HBM-bound workloads are timed cold (COLD_COPIES input copies in
+            # rotation); the others warm, inputs reused from launch to launch
+            cold = bound == "hbm"
+            if isinstance(case, I.PagedPrefillCase):
+                r = PagedRun(torch, case)
+            else:
+                r = VarlenRun(torch, case, copies=COLD_COPIES if cold else 1)
             _, t = time_launches(torch, r, 20, 3)
             dense = case.dense if isinstance(case, I.PagedPrefillCase) else case
             f, b = I.varlen_flops(dense), I.varlen_bytes(dense)
             ctx[name] = {"avg_us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 2),
                          "frac_mfma_peak": round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "GB/s": round(b / t / 1e9, 1), "frac_hbm_peak": round(b / t / 1e9 / PEAK_HBM_GBS, 4),
-                         "bound": bound}
+                         "bound": bound, "cold": cold}
+            if cold:
+                ctx[name]["copies"] = COLD_COPIES
             del r
+            torch.cuda.empty_cache()
         lines["other_workloads"] = ctx
 
     if not args.no_cpu_baseline:
