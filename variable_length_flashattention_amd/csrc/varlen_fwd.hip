@@ -342,31 +342,49 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                 // each V row by exactly what the MMA used (with the fp32 sum a
                 // dominant weight above 1 would be off by its rounding, up to
                 // 2^-9 |v|).
-                // The scores go in chunks of 8 (8 independent FMAs, then 8
-                // independent exponentials), and the sums run in 4 + 2 partial
-                // accumulators, so that a wave alone on its SIMD's VALU is not
-                // held up by the latency of one long dependency chain.
+                // At head_dim >= 128 the scores go in chunks of 8 (8 independent
+                // FMAs, then 8 independent exponentials) and the sums run in
+                // 4 + 2 partial accumulators, so that a wave alone on its
+                // SIMD's VALU is not held up by one long dependency chain; at
+                // head_dim 64, where three workgroups share a CU's registers,
+                // a pair at a time.
                 float rb = 0.f;
                 auto probs = [&](float mc) __attribute__((always_inline)) -> float {
-                    float rs4[4], rb2[2] = {0.f, 0.f};
+                    if constexpr (D >= 128) {
+                        float rs4[4], rb2[2] = {0.f, 0.f};
 #pragma unroll
-                    for (int q = 0; q < 2 * NC; q++) {
-                        const int c = q >> 1, base = 8 * (q & 1);
-                        float t[8];
+                        for (int q = 0; q < 2 * NC; q++) {
+                            const int c = q >> 1, base = 8 * (q & 1);
+                            float t[8];
 #pragma unroll
-                        for (int i = 0; i < 8; i++) t[i] = fmaf(s[u][c][base + i], sl2, -mc);
+                            for (int i = 0; i < 8; i++) t[i] = fmaf(s[u][c][base + i], sl2, -mc);
 #pragma unroll
-                        for (int i = 0; i < 8; i++) t[i] = fast_exp2(t[i]);
+                            for (int i = 0; i < 8; i++) t[i] = fast_exp2(t[i]);
 #pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            const uint32_t pair = pack_bf16x2(t[2 * i], t[2 * i + 1]);
-                            pk[u][c][base / 2 + i] = pair;
-                            rs4[i] = q == 0 ? t[2 * i] + t[2 * i + 1] : rs4[i] + (t[2 * i] + t[2 * i + 1]);
-                            rb2[i & 1] = add_bf16x2(pair, rb2[i & 1]);
+                            for (int i = 0; i < 4; i++) {
+                                const uint32_t pair = pack_bf16x2(t[2 * i], t[2 * i + 1]);
+                                pk[u][c][base / 2 + i] = pair;
+                                rs4[i] = q == 0 ? t[2 * i] + t[2 * i + 1] : rs4[i] + (t[2 * i] + t[2 * i + 1]);
+                                rb2[i & 1] = add_bf16x2(pair, rb2[i & 1]);
+                            }
                         }
+                        rb = rb2[0] + rb2[1];
+                        return (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+                    } else {
+                        float rs = 0.f;
+                        rb = 0.f;
+#pragma unroll
+                        for (int c = 0; c < NC; c++)
+#pragma unroll
+                            for (int r2 = 0; r2 < 8; r2++) {
+                                const float p0 = fast_exp2(fmaf(s[u][c][2 * r2], sl2, -mc));
+                                const float p1 = fast_exp2(fmaf(s[u][c][2 * r2 + 1], sl2, -mc));
+                                pk[u][c][r2] = pack_bf16x2(p0, p1);
+                                rs += p0 + p1;
+                                rb = add_bf16x2(pk[u][c][r2], rb);
+                            }
+                        return rs;
                     }
-                    rb = rb2[0] + rb2[1];
-                    return (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
                 };
                 float rs = 0.f;
                 bool slow = __builtin_amdgcn_ballot_w64(m_ref[u] == -INFINITY) != 0;
