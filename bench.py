@@ -276,6 +276,12 @@ def cpu_baseline(case, n_rows=655360, seed=7):
                       f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, fp64"}
 
 
+# profiles/<record>_hbm_traffic.json for the context workloads that have one
+TRAFFIC_RECORDS = {"skewed": "varlen_fwd_skewed", "chunked_paged_bs16": "varlen_fwd_paged_chunked_bs16",
+                   "many_short_d64_causal": "varlen_fwd_many_short_d64",
+                   "many_short_d256_causal": "varlen_fwd_many_short_d256"}
+
+
 def load_traffic(name, src_hash):
     """HBM bytes per launch measured with rocprofv3 counters (scaled by a copy
     kernel calibration), if the record matches the current kernel sources."""
@@ -438,6 +444,8 @@ def main():
                          "frac_mfma_peak": round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "GB/s": round(b / t / 1e9, 1), "frac_hbm_peak": round(b / t / 1e9 / PEAK_HBM_GBS, 4),
                          "bound": bound, "cold": cold}
+            if name in TRAFFIC_RECORDS:
+                ctx[name]["traffic"] = load_traffic(TRAFFIC_RECORDS[name], kernel_source_hash(VARLEN_SOURCES))
             if cold:
                 ctx[name]["copies"] = COLD_COPIES
             del r
