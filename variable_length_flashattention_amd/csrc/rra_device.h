@@ -51,6 +51,10 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __builtin_bi
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and leaves the other counters alone.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Raw buffer descriptor over `base` (byte addressing, no stride, 2^31-1 bytes
 // in range; the data-format field is the one the CDNA buffer loads expect).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base)

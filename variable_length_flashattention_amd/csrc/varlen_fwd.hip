@@ -89,6 +89,70 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
     const WorkTables wt = build_work_tables(a.cu_q, kcount, PAGED ? a.batch : a.batch + 1, a.batch, BQ, a.levels,
                                             sched, kSchedInts);
 
+    // Output stores.  The accumulators hold O^T, 4 consecutive d of one query
+    // per register quad, so stores straight from them would write 8-byte
+    // pieces of 32 rows per instruction.  Instead each wave writes its rows
+    // (bf16) to a private LDS slot and reads them back so that consecutive
+    // lanes hold consecutive 16-byte pieces of a row: every store then writes
+    // whole 128-d row segments.  NST store instructions go out per item (lanes
+    // with nothing to store get an offset past the buffer's range, and the
+    // hardware drops those writes).
+    // At head_dim <= 128 the slots are in the K/V buffer the item's last tile
+    // did not use, and the rows are stored at once.  At head_dim 256 they do
+    // not fit there; the slots are an array of their own, and the stores are
+    // held back until the next item's first loads are issued: the load/store
+    // counter retires in order, so stores issued before those loads would
+    // have to be written out before the next item's first key tile could
+    // start, and with a constant NST the wait there can leave exactly the NST
+    // youngest operations in flight.  (Holding back at head_dim <= 128 needs
+    // the slots in the second buffer, and with an even number of tiles a
+    // barrier before writing them: measured slower on gfx950 than storing at
+    // once, while at head_dim 256 holding back is 5 % faster.)
+    static_assert(RPW == 1, "the slot stores cover one 32-row block per wave");
+    constexpr int CW = D < 128 ? D : 128;  // d columns per row segment
+    constexpr int RB = D * 2;              // slot bytes per row
+    constexpr int CHR = CW / 8;            // 16-byte chunks per row segment
+    constexpr int SLOT = 32 * RB;
+    constexpr int RPI = 64 / CHR;          // rows per read (and store) instruction
+    constexpr int NPASS = D / CW, NRD = 32 / RPI;
+    constexpr int NST = NPASS * NRD + 1;   // store instructions per item: out rows, then lse
+    constexpr bool DEFER = 2 * SLOT > TB;  // own slots, stores held back to the next item
+    __shared__ __attribute__((aligned(1024))) uint8_t o_lds[DEFER ? NW * SLOT : 16];
+    constexpr uint32_t kDrop = 0x80000000u;  // a buffer offset past the range: the write is dropped
+    float pend_lse_v = 0.f;
+    uint16_t *pend_out = a.out;
+    float *pend_lse = a.lse;
+    int pend_n = 0;  // rows of the block to store (0: nothing)
+    // chunk c of a slot row r sits at physical chunk c ^ (r & 7): the 8-byte
+    // writes (32 rows, one chunk) and the 16-byte reads (RPI rows) are then
+    // spread evenly over the banks
+    auto flush_from = [&](const uint8_t *slot) __attribute__((always_inline)) {
+        int lid = lane;
+        __asm__ volatile("" : "+v"(lid));
+        const __amdgpu_buffer_rsrc_t ob = raw_buffer(pend_out), lb = raw_buffer(pend_lse);
+        const uint32_t rstride = (uint32_t)H * D * 2;
+        // all slot reads first, then the stores (one LDS round trip, not one per store)
+        u32x4 val[NPASS][NRD];
+#pragma unroll
+        for (int p = 0; p < NPASS; p++)
+#pragma unroll
+            for (int i = 0; i < NRD; i++) {
+                const int r = i * RPI + lid / CHR, c = p * CHR + lid % CHR;
+                val[p][i] = *reinterpret_cast<const u32x4 *>(slot + r * RB + 16 * (c ^ (r & 7)));
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < NPASS; p++)
+#pragma unroll
+            for (int i = 0; i < NRD; i++) {
+                const int r = i * RPI + lid / CHR, c = p * CHR + lid % CHR;
+                const uint32_t off = r < pend_n ? r * rstride + 16 * c : kDrop;
+                __builtin_amdgcn_raw_buffer_store_b128(val[p][i], ob, off, 0, 0);
+            }
+        const uint32_t loff = (lid < 32 && lid < pend_n) ? (uint32_t)(lid * H * 4) : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pend_lse_v), lb, loff, 0, 0);
+    };
+
     // persistent workgroups: items are dealt out in serpentine order
     for (int64_t k = 0;; k++) {
         const int64_t w = serpentine_item(k, blockIdx.x, gridDim.x);
@@ -237,6 +301,12 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
 #pragma unroll
             for (int ks = 0; ks < NKS; ks++) qf[u][ks] = as_bf16x8(load16(qrow + 16 * ks));
         }
+        if constexpr (DEFER) {
+            // the previous item's stores, behind this item's first loads
+            __builtin_amdgcn_sched_barrier(0);
+            flush_from(o_lds + wave * SLOT);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         f32x16 o[RPW][NDC];
 #pragma unroll
         for (int u = 0; u < RPW; u++)
@@ -261,7 +331,12 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         // staged into the buffer tile kt-1 used
         auto tile = [&](int kt, const uint8_t *Kb, const uint8_t *Vb, uint8_t *kn, uint8_t *vn) {
             const int kbase = kt * BK;
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt are done
+            // this wave's loads of tile kt are done (at the first tile, the
+            // previous item's NST stores, issued last, may stay in flight)
+            // (the builtin, unlike inline asm, is known to the compiler's own
+            // wait placement, which then counts the first loads as done)
+            if (DEFER && kt == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __syncthreads();  // tile kt visible; every wave is done with tile kt-1
             if (kt + 1 < nkt) stage(kt + 1, kn, vn);
             bool act[RPW];
@@ -451,30 +526,64 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                 }
             }
         };
-        for (int kt = 0; kt < nkt; kt += 2) {
-            tile(kt, k_lds0, v_lds0, k_lds1, v_lds1);
-            if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        if constexpr (DEFER) {
+            // The first tile is peeled off the loop: the compiler waits for
+            // every load and store in flight before a loop that uses registers
+            // loaded ahead of it (the Q fragments), and that wait then comes
+            // after the first tile, where the loads of the second are due
+            // anyway, instead of holding the first tile up until the previous
+            // item's stores are written.
+            if (nkt > 0) {
+                tile(0, k_lds0, v_lds0, k_lds1, v_lds1);
+                for (int kt = 1; kt < nkt; kt += 2) {
+                    tile(kt, k_lds1, v_lds1, k_lds0, v_lds0);
+                    if (kt + 1 < nkt) tile(kt + 1, k_lds0, v_lds0, k_lds1, v_lds1);
+                }
+            }
+        } else {
+            for (int kt = 0; kt < nkt; kt += 2) {
+                tile(kt, k_lds0, v_lds0, k_lds1, v_lds1);
+                if (kt + 1 < nkt) tile(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+            }
         }
 
-        // epilogue: out = O / l_mma (0 when no key is visible), lse = scale*m + ln l_run (-inf then)
-#pragma unroll
-        for (int u = 0; u < RPW; u++) {
-            if (!row_ok[u]) continue;
-            const float inv_l = l_run[u] > 0.f ? 1.f / l_mma[u] : 0.f;
-            uint16_t *orow = a.out + ((int64_t)(q0 + my_i[u]) * H + h) * D + 4 * (lane >> 5);
+        // epilogue: out = O / l_mma (0 when no key is visible), lse = scale*m + ln l_run (-inf then),
+        // as bf16 rows in the wave's slot; chunk c of a slot row r sits at
+        // physical chunk c ^ (r & 7), so that the 8-byte writes (32 rows, one
+        // chunk) and the 16-byte reads (RPI rows) spread evenly over the banks
+        auto to_slot = [&](uint8_t *slot) __attribute__((always_inline)) {
+            int lid = lane;
+            __asm__ volatile("" : "+v"(lid));
+            const int wrow = lid & 31, half = lid >> 5;
+            const float inv_l = l_run[0] > 0.f ? 1.f / l_mma[0] : 0.f;
 #pragma unroll
             for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
                 for (int rb4 = 0; rb4 < 4; rb4++) {
-                    const u32x2 pr = {pack_bf16x2(o[u][dc][4 * rb4] * inv_l, o[u][dc][4 * rb4 + 1] * inv_l),
-                                      pack_bf16x2(o[u][dc][4 * rb4 + 2] * inv_l, o[u][dc][4 * rb4 + 3] * inv_l)};
-                    *reinterpret_cast<u32x2 *>(orow + 32 * dc + 8 * rb4) = pr;
+                    const u32x2 pr = {pack_bf16x2(o[0][dc][4 * rb4] * inv_l, o[0][dc][4 * rb4 + 1] * inv_l),
+                                      pack_bf16x2(o[0][dc][4 * rb4 + 2] * inv_l, o[0][dc][4 * rb4 + 3] * inv_l)};
+                    const int ch = (4 * dc + rb4) ^ (wrow & 7);
+                    *reinterpret_cast<u32x2 *>(slot + wrow * RB + 16 * ch + 8 * half) = pr;
                 }
-            if (lane < 32)
-                a.lse[(int64_t)(q0 + my_i[u]) * H + h] =
-                    l_run[u] > 0.f ? a.scale * m_ref[u] + logf(l_run[u]) : -INFINITY;
+        };
+        pend_lse_v = l_run[0] > 0.f ? a.scale * m_ref[0] + logf(l_run[0]) : -INFINITY;
+        pend_out = a.out + ((int64_t)(q0 + iw[0]) * H + h) * D;
+        pend_lse = a.lse + (int64_t)(q0 + iw[0]) * H + h;
+        pend_n = max(0, min(32, nrows - 32 * wave));
+        if constexpr (DEFER) {
+            to_slot(o_lds + wave * SLOT);
+        } else {
+            // the K/V buffer the last tile, nkt - 1, did not use: no load is in
+            // flight into it, and the next item stages into it only after the
+            // barrier at the item's start
+            uint8_t *kfree = (nkt & 1) ? k_lds1 : k_lds0, *vfree = (nkt & 1) ? v_lds1 : v_lds0;
+            uint8_t *slot = ((wave & 2) ? vfree : kfree) + (wave & 1) * SLOT;
+            to_slot(slot);
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in the slot
+            flush_from(slot);
         }
     }
+    if constexpr (DEFER) flush_from(o_lds + wave * SLOT);  // the last item's stores
 }
 
 // Test hook: the same work tables and decoder, one wave per workgroup.
