@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="skip the context workloads")
-    p.add_argument("--only", default="", choices=["", "mixed", "decode", "skewed", "many_short_d64",
+    p.add_argument("--only", default="", choices=["", "mixed", "decode", "decode_steps", "skewed", "many_short_d64",
                                                   "many_short_d256", "chunked_paged_bs16", "backward"],
                    help="time only this workload (for profiling runs)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -315,7 +315,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.only and args.only != "mixed":
-        case = {"decode": None, "skewed": I.skewed(), "many_short_d64": I.many_short(64, True),
+        case = {"decode": None, "decode_steps": "steps", "skewed": I.skewed(), "many_short_d64": I.many_short(64, True),
                 "many_short_d256": I.many_short(256, True), "chunked_paged_bs16": "paged",
                 "backward": "backward"}[args.only]
         if case == "backward":
@@ -326,9 +326,10 @@ def main():
             case = I.chunked_paged(16)
             r = PagedRun(torch, case)
             nbytes, flops = I.varlen_bytes(case.dense), I.varlen_flops(case.dense)
-        elif case is None:
+        elif case is None or case == "steps":
+            steps = case == "steps"
             case = I.paged_decode()
-            r = DecodeRun(torch, case, copies=DECODE_COPIES)
+            r = (DecodeStepsRun if steps else DecodeRun)(torch, case, copies=DECODE_COPIES)
             nbytes, flops = I.decode_bytes(case), I.decode_flops(case)
         else:
             hbm_bound = args.only.startswith("many_short")
