@@ -12,11 +12,24 @@
  *     call launches nothing and returns a status below.  Launch failures
  *     reported by the HIP runtime return RRA_ERR_HIP.  No C++ exception
  *     crosses this boundary.
- *   - The library keeps no device allocations of its own: the caller owns
- *     every buffer (outputs and the decode workspace included).
+ *   - The library allocates no device memory: the caller owns every buffer
+ *     (outputs and workspaces included).  Two static device arrays live in
+ *     the library itself: the allocation-free decode's scratch and the
+ *     one-word verdict of the debug check below.
  *   - The contents of device-side index arrays (cu_seqlens, block tables,
  *     context lengths) are preconditions, as stated per entry point; they are
  *     not read on the host.
+ *   - Debug check: with RRA_VALIDATE=1 in the environment, the forward
+ *     (packed, GQA, paged), backward and pack/unpack calls first check their
+ *     sequence offsets on the device ([PLAN] Task 1 leaves these
+ *     preconditions to the caller) and, launching nothing else, return
+ *     RRA_ERR_INVALID_ARG when cu_seqlens[0] != 0, a sequence length is
+ *     negative or above max_seqlen_q (max_seqlen_k for the backward's keys,
+ *     max_seqlen for pack/unpack), the backward's cu_seqlens_q[batch] exceeds
+ *     total_q, or a paged key length lies outside
+ *     [0, max_blocks_per_seq * block_size].  The check is one small kernel
+ *     and a synchronisation of `stream` per call; without the variable
+ *     nothing is checked and nothing synchronises.
  *
  * Sources are cited by page title and section:
  *   [PLAN]   "Varlen Flash Attention Implementation Plan" (rustytorch)

@@ -2,6 +2,7 @@
 // kernel launch.  Validation happens before any HIP call; rejected calls
 // launch nothing.
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <mutex>
 
@@ -67,6 +68,57 @@ void *scratch_ptr()
     return ptrs[dev];
 }
 
+// Debug check of the sequence offsets, run when the environment holds
+// RRA_VALIDATE=1 (the preconditions of "Varlen Flash Attention
+// Implementation Plan", Task 1, are otherwise the caller's to keep):
+// cu_q[0] == 0, every Lq in [0, max_q] and cu_q[batch] <= total_q (when
+// total_q >= 0); the keys likewise as offsets (every Lk >= 0, and <= max_k
+// when max_k >= 0), or, for paged keys, as per-sequence lengths in
+// [0, k_cap].  One workgroup writes its verdict (0 or 1) to a static device
+// word, which the host reads back, so the check synchronises the stream.
+__device__ int32_t cu_check_bad;
+
+__global__ __launch_bounds__(256) void cu_check_kernel(const int32_t *cu_q, const int32_t *k, int32_t batch,
+                                                       int32_t max_q, int64_t total_q, int32_t max_k,
+                                                       int32_t k_lens, int32_t k_cap)
+{
+    int bad = 0;
+    if (threadIdx.x == 0) {
+        bad |= cu_q[0] != 0 || (!k_lens && k[0] != 0);
+        bad |= total_q >= 0 && (int64_t)cu_q[batch] > total_q;
+    }
+    for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+        const int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b];
+        bad |= lq < 0 || lq > max_q;
+        const int64_t lk = k_lens ? (int64_t)k[b] : (int64_t)k[b + 1] - k[b];
+        bad |= lk < 0 || (k_lens ? lk > k_cap : (max_k >= 0 && lk > max_k));
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) cu_check_bad = bad;
+}
+
+bool validate_requested()
+{
+    const char *e = std::getenv("RRA_VALIDATE");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+int32_t check_offsets(const int32_t *cu_q, const int32_t *k, int32_t batch, int32_t max_q, int64_t total_q,
+                      int32_t max_k, bool k_lens, int32_t k_cap, void *stream)
+{
+    if (!validate_requested()) return RRA_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(cu_check_kernel, dim3(1), dim3(256), 0, st, cu_q, k, batch, max_q, total_q, max_k,
+                       (int32_t)k_lens, k_cap);
+    if (hipGetLastError() != hipSuccess) return RRA_ERR_HIP;
+    int32_t bad = 1;
+    if (hipMemcpyFromSymbolAsync(&bad, HIP_SYMBOL(cu_check_bad), sizeof bad, 0, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return RRA_ERR_HIP;
+    return bad ? RRA_ERR_INVALID_ARG : RRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +155,9 @@ int32_t rra_varlen_attn_fwd_gqa(const void *q, const void *k, const void *v, voi
     if (!q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k) return RRA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
         return RRA_ERR_INVALID_ARG;
+
+    const int32_t vrc = check_offsets(cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, -1, -1, false, 0, stream);
+    if (vrc != RRA_OK) return vrc;
 
     VarlenArgs a;
     a.q = static_cast<const uint16_t *>(q);
@@ -150,6 +205,10 @@ int32_t rra_varlen_attn_fwd_paged(const void *q, const void *k_pool, const void 
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u))
         return RRA_ERR_INVALID_ARG;
+
+    const int32_t vrc = check_offsets(cu_seqlens_q, seqlens_k, batch, max_seqlen_q, -1, -1, true,
+                                      max_blocks_per_seq * block_size, stream);
+    if (vrc != RRA_OK) return vrc;
 
     VarlenArgs a;
     a.q = static_cast<const uint16_t *>(q);
@@ -215,6 +274,10 @@ int32_t rra_varlen_attn_bwd(const void *q, const void *k, const void *v, const v
     const size_t need = rra_varlen_attn_bwd_workspace_bytes(total_q, num_heads);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return RRA_ERR_WORKSPACE;
 
+    const int32_t vrc =
+        check_offsets(cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, total_q, max_seqlen_k, false, 0, stream);
+    if (vrc != RRA_OK) return vrc;
+
     BwdArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -255,6 +318,8 @@ static int32_t pack_call(const void *src, void *dst, const int32_t *cu_seqlens, 
     const int64_t rows = pack_rows_per_wg(row_bytes);
     const int64_t wgs = (int64_t)batch * ((max_seqlen + rows - 1) / rows);
     if (wgs > INT32_MAX || row_bytes / 4 > INT32_MAX) return RRA_ERR_INVALID_ARG;
+    const int32_t vrc = check_offsets(cu_seqlens, cu_seqlens, batch, max_seqlen, -1, -1, false, 0, stream);
+    if (vrc != RRA_OK) return vrc;
     const bool vec16 = row_bytes % 16 == 0 && aligned16(src) && aligned16(dst);
     return hip_status(launch_pack_rows(src, dst, cu_seqlens, batch, max_seqlen, row_bytes, to_packed, vec16,
                                        static_cast<hipStream_t>(stream)));
