@@ -39,10 +39,10 @@
 
 namespace rra {
 
-template <int D, int RPW>
+template <int D>
 struct VarlenTile {
     static constexpr int NW = 4;                       // waves per workgroup
-    static constexpr int BQ = 32 * NW * RPW;           // query rows per work item
+    static constexpr int BQ = 32 * NW;                 // query rows per work item (32 per wave)
     static constexpr int BK = D <= 128 ? 64 : 32;
     static constexpr int NBUF = 2;                     // K/V tile buffers (one in flight, one in use)
     static constexpr int ROWB = D * 2;                 // bytes per K/V row
@@ -57,14 +57,14 @@ struct VarlenTile {
     __device__ static int swz_v(int row) { return 2 * (row & 3); }
     static constexpr int THREADS = 64 * NW;
     // workgroups per CU: three at head_dim 64, two at 128 (256 VGPRs each),
-    // one at 256; 64 rows per wave: one, accumulators in AGPRs
-    static constexpr int MIN_BLOCKS = RPW == 1 ? (D == 64 ? 3 : D == 128 ? 2 : 1) : 1;
+    // one at 256
+    static constexpr int MIN_BLOCKS = D == 64 ? 3 : D == 128 ? 2 : 1;
 };
 
-template <int D, bool CAUSAL, bool PAGED, int RPW>
-__global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>::MIN_BLOCKS)) void varlen_fwd_kernel(VarlenArgs a)
+template <int D, bool CAUSAL, bool PAGED>
+__global__ __launch_bounds__((VarlenTile<D>::THREADS), (VarlenTile<D>::MIN_BLOCKS)) void varlen_fwd_kernel(VarlenArgs a)
 {
-    using T = VarlenTile<D, RPW>;
+    using T = VarlenTile<D>;
     constexpr int NW = T::NW, BQ = T::BQ, BK = T::BK, ROWB = T::ROWB, TB = T::TILE_BYTES;
     constexpr int NC = BK / 32;          // 32-key accumulator tiles per key tile
     constexpr int NKS = D / 16;          // k-steps of the QK^T MMA
@@ -108,7 +108,6 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
     // the slots in the second buffer, and with an even number of tiles a
     // barrier before writing them: measured slower on gfx950 than storing at
     // once, while at head_dim 256 holding back is 5 % faster.)
-    static_assert(RPW == 1, "the slot stores cover one 32-row block per wave");
     constexpr int CW = D < 128 ? D : 128;  // d columns per row segment
     constexpr int RB = D * 2;              // slot bytes per row
     constexpr int CHR = CW / 8;            // 16-byte chunks per row segment
@@ -184,20 +183,13 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         if (CAUSAL) kend = max(0, min(Lk, i0 + nrows + diag));
         const int nkt = (kend + BK - 1) / BK;
 
-        // This wave owns RPW blocks of 32 rows: rows i0 + 32*(RPW*wave + u) + lane%32.
-        int iw[RPW], my_i[RPW], nkt_u[RPW];
-        bool row_ok[RPW];
-#pragma unroll
-        for (int u = 0; u < RPW; u++) {
-            const int blk = RPW * wave + u;
-            iw[u] = i0 + 32 * blk;
-            my_i[u] = iw[u] + (lane & 31);
-            row_ok[u] = my_i[u] < Lq;
-            int kend_u = Lk;
-            if (CAUSAL) kend_u = max(0, min(Lk, min(iw[u] + 31, Lq - 1) + 1 + diag));
-            if (32 * blk >= nrows) kend_u = 0;
-            nkt_u[u] = (kend_u + BK - 1) / BK;
-        }
+        // This wave owns rows i0 + 32*wave + lane%32 and needs key tiles 0..nkt_w-1.
+        const int iw = i0 + 32 * wave;
+        const int my_i = iw + (lane & 31);
+        int kend_w = Lk;
+        if (CAUSAL) kend_w = max(0, min(Lk, min(iw + 31, Lq - 1) + 1 + diag));
+        if (32 * wave >= nrows) kend_w = 0;
+        const int nkt_w = (kend_w + BK - 1) / BK;
 
         // Direct-to-LDS staging of key tile kt with buffer loads: the tile's
         // first row is the buffer base (64-bit, scalar), each load adds a
@@ -293,13 +285,12 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
         // Q^T operand: lane holds Q[my_i][16*ks + 8*(lane/32) .. +7]
         // (rows past the sequence end read its last row; their results are
         // never stored, and an unconditional load is not waited on at once)
-        bf16x8 qf[RPW][NKS];
-#pragma unroll
-        for (int u = 0; u < RPW; u++) {
-            const int qr = min(my_i[u], Lq - 1);
+        bf16x8 qf[NKS];
+        {
+            const int qr = min(my_i, Lq - 1);
             const uint16_t *qrow = a.q + ((int64_t)(q0 + qr) * H + h) * D + 8 * (lane >> 5);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ks++) qf[u][ks] = as_bf16x8(load16(qrow + 16 * ks));
+            for (int ks = 0; ks < NKS; ks++) qf[ks] = as_bf16x8(load16(qrow + 16 * ks));
         }
         if constexpr (DEFER) {
             // the previous item's stores, behind this item's first loads
@@ -307,25 +298,17 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             flush_from(o_lds + wave * SLOT);
             __builtin_amdgcn_sched_barrier(0);
         }
-        f32x16 o[RPW][NDC];
+        f32x16 o[NDC];
 #pragma unroll
-        for (int u = 0; u < RPW; u++)
+        for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
-            for (int dc = 0; dc < NDC; dc++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) o[u][dc][r] = 0.f;
+            for (int r = 0; r < 16; r++) o[dc][r] = 0.f;
         // m_ref: the max the accumulators are currently scaled to; it is only
         // raised when a tile's probabilities against it grow too large (a
         // lane's share of a row sum above 2^15), which skips most row-max
         // reductions and rescales of O.  l_run sums the fp32 probabilities
         // (for lse), l_mma the bf16 values the PV MMA takes (for out).
-        float m_ref[RPW], l_run[RPW], l_mma[RPW];
-#pragma unroll
-        for (int u = 0; u < RPW; u++) {
-            m_ref[u] = -INFINITY;
-            l_run[u] = 0.f;
-            l_mma[u] = 0.f;
-        }
+        float m_ref = -INFINITY, l_run = 0.f, l_mma = 0.f;
 
         // one key tile; tile kt lives in buffer kt % 2, and tile kt+1 is
         // staged into the buffer tile kt-1 used
@@ -339,23 +322,14 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __syncthreads();  // tile kt visible; every wave is done with tile kt-1
             if (kt + 1 < nkt) stage(kt + 1, kn, vn);
-            bool act[RPW];
-            bool any = false;
-#pragma unroll
-            for (int u = 0; u < RPW; u++) {
-                act[u] = kt < nkt_u[u];
-                any |= act[u];
-            }
-            if (!any) return;
+            if (kt >= nkt_w) return;  // the wave's rows see no key of this tile
 
-            // S^T = K Q^T; each K operand read feeds every active row block
-            f32x16 s[RPW][NC];
+            // S^T = K Q^T
+            f32x16 s[NC];
 #pragma unroll
-            for (int u = 0; u < RPW; u++)
+            for (int c = 0; c < NC; c++)
 #pragma unroll
-                for (int c = 0; c < NC; c++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) s[u][c][r] = 0.f;
+                for (int r = 0; r < 16; r++) s[c][r] = 0.f;
             // K fragments are read KD MMAs ahead of use; the scheduling
             // barriers keep the compiler from sinking the reads next to
             // their MMAs (it does that under register pressure, and each
@@ -382,27 +356,23 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                     const bf16x8 ka = kf[m % KD];
                     if (m + KD < NM) kf[m % KD] = kread(m + KD);
                     const int c = m / NKS, ks = m % NKS;
-#pragma unroll
-                    for (int u = 0; u < RPW; u++)
-                        if (act[u]) s[u][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[u][ks], s[u][c], 0, 0, 0);
+                    s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[c], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
             __builtin_amdgcn_s_setprio(0);
-            uint32_t pk[RPW][NC][8];
-#pragma unroll
-            for (int u = 0; u < RPW; u++) {
-                if (!act[u]) continue;
+            uint32_t pk[NC][8];
+            {
                 // tail and causal masks (only tiles that need them)
-                const bool need_mask = (kbase + BK > Lk) || (CAUSAL && kbase + BK - 1 > iw[u] + diag);
+                const bool need_mask = (kbase + BK > Lk) || (CAUSAL && kbase + BK - 1 > iw + diag);
                 if (need_mask) {
-                    const int last = CAUSAL ? min(Lk - 1, my_i[u] + diag) : Lk - 1;
+                    const int last = CAUSAL ? min(Lk - 1, my_i + diag) : Lk - 1;
 #pragma unroll
                     for (int c = 0; c < NC; c++)
 #pragma unroll
                         for (int r = 0; r < 16; r++) {
                             const int key = kbase + 32 * c + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                            if (key > last) s[u][c][r] = -INFINITY;
+                            if (key > last) s[c][r] = -INFINITY;
                         }
                 }
                 // online softmax (row = this lane's query; lanes l and l^32 share it).
@@ -432,13 +402,13 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                             const int c = q >> 1, base = 8 * (q & 1);
                             float t[8];
 #pragma unroll
-                            for (int i = 0; i < 8; i++) t[i] = fmaf(s[u][c][base + i], sl2, -mc);
+                            for (int i = 0; i < 8; i++) t[i] = fmaf(s[c][base + i], sl2, -mc);
 #pragma unroll
                             for (int i = 0; i < 8; i++) t[i] = fast_exp2(t[i]);
 #pragma unroll
                             for (int i = 0; i < 4; i++) {
                                 const uint32_t pair = pack_bf16x2(t[2 * i], t[2 * i + 1]);
-                                pk[u][c][base / 2 + i] = pair;
+                                pk[c][base / 2 + i] = pair;
                                 rs4[i] = q == 0 ? t[2 * i] + t[2 * i + 1] : rs4[i] + (t[2 * i] + t[2 * i + 1]);
                                 rb2[i & 1] = add_bf16x2(pair, rb2[i & 1]);
                             }
@@ -452,19 +422,19 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                         for (int c = 0; c < NC; c++)
 #pragma unroll
                             for (int r2 = 0; r2 < 8; r2++) {
-                                const float p0 = fast_exp2(fmaf(s[u][c][2 * r2], sl2, -mc));
-                                const float p1 = fast_exp2(fmaf(s[u][c][2 * r2 + 1], sl2, -mc));
-                                pk[u][c][r2] = pack_bf16x2(p0, p1);
+                                const float p0 = fast_exp2(fmaf(s[c][2 * r2], sl2, -mc));
+                                const float p1 = fast_exp2(fmaf(s[c][2 * r2 + 1], sl2, -mc));
+                                pk[c][r2] = pack_bf16x2(p0, p1);
                                 rs += p0 + p1;
-                                rb = add_bf16x2(pk[u][c][r2], rb);
+                                rb = add_bf16x2(pk[c][r2], rb);
                             }
                         return rs;
                     }
                 };
                 float rs = 0.f;
-                bool slow = __builtin_amdgcn_ballot_w64(m_ref[u] == -INFINITY) != 0;
+                bool slow = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
                 if (!slow) {
-                    rs = probs(m_ref[u] * sl2);
+                    rs = probs(m_ref * sl2);
                     slow = __builtin_amdgcn_ballot_w64(!(rs <= 32768.f)) != 0;  // (also catches inf)
                 }
                 if (slow) {
@@ -472,27 +442,26 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
 #pragma unroll
                     for (int c = 0; c < NC; c++)
 #pragma unroll
-                        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[u][c][r], s[u][c][r + 1]);
+                        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[c][r], s[c][r + 1]);
                     mx = max_across_halves(mx);
-                    const float m_new = fmaxf(m_ref[u], mx);
+                    const float m_new = fmaxf(m_ref, mx);
                     const float alpha =
-                        (m_ref[u] == -INFINITY || m_new == m_ref[u]) ? 1.f : fast_exp2((m_ref[u] - m_new) * sl2);
-                    l_run[u] *= alpha;
-                    l_mma[u] *= alpha;
+                        (m_ref == -INFINITY || m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+                    l_run *= alpha;
+                    l_mma *= alpha;
 #pragma unroll
                     for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
-                        for (int r = 0; r < 16; r++) o[u][dc][r] *= alpha;
-                    m_ref[u] = m_new;
+                        for (int r = 0; r < 16; r++) o[dc][r] *= alpha;
+                    m_ref = m_new;
                     rs = probs((m_new == -INFINITY ? 0.f : m_new) * sl2);
                 }
-                l_run[u] += sum_across_halves(rs);
-                l_mma[u] += sum_across_halves(rb);
+                l_run += sum_across_halves(rs);
+                l_mma += sum_across_halves(rb);
             }
 
-            // O^T += V^T P^T, 16 keys per MMA; each V operand read feeds every
-            // active row block
-            // V^T fragments (two transposed reads each) read VD MMAs ahead of use
+            // O^T += V^T P^T, 16 keys per MMA; V^T fragments (two transposed
+            // reads each) read VD MMAs ahead of use
             const int g = lane >> 4, j = lane & 15;
             {
                 constexpr int NM = (BK / 16) * NDC, VD = 3;
@@ -515,13 +484,9 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
                     const u32x4 vv = vf[mm % VD];
                     if (mm + VD < NM) vf[mm % VD] = vread(mm + VD);
                     const int m = mm / NDC, dc = mm % NDC;
-#pragma unroll
-                    for (int u = 0; u < RPW; u++) {
-                        const u32x4 pb = {pk[u][m >> 1][4 * (m & 1) + 0], pk[u][m >> 1][4 * (m & 1) + 1],
-                                          pk[u][m >> 1][4 * (m & 1) + 2], pk[u][m >> 1][4 * (m & 1) + 3]};
-                        if (act[u])
-                            o[u][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), o[u][dc], 0, 0, 0);
-                    }
+                    const u32x4 pb = {pk[m >> 1][4 * (m & 1) + 0], pk[m >> 1][4 * (m & 1) + 1],
+                                      pk[m >> 1][4 * (m & 1) + 2], pk[m >> 1][4 * (m & 1) + 3]};
+                    o[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), o[dc], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -555,20 +520,20 @@ __global__ __launch_bounds__((VarlenTile<D, RPW>::THREADS), (VarlenTile<D, RPW>:
             int lid = lane;
             __asm__ volatile("" : "+v"(lid));
             const int wrow = lid & 31, half = lid >> 5;
-            const float inv_l = l_run[0] > 0.f ? 1.f / l_mma[0] : 0.f;
+            const float inv_l = l_run > 0.f ? 1.f / l_mma : 0.f;
 #pragma unroll
             for (int dc = 0; dc < NDC; dc++)
 #pragma unroll
                 for (int rb4 = 0; rb4 < 4; rb4++) {
-                    const u32x2 pr = {pack_bf16x2(o[0][dc][4 * rb4] * inv_l, o[0][dc][4 * rb4 + 1] * inv_l),
-                                      pack_bf16x2(o[0][dc][4 * rb4 + 2] * inv_l, o[0][dc][4 * rb4 + 3] * inv_l)};
+                    const u32x2 pr = {pack_bf16x2(o[dc][4 * rb4] * inv_l, o[dc][4 * rb4 + 1] * inv_l),
+                                      pack_bf16x2(o[dc][4 * rb4 + 2] * inv_l, o[dc][4 * rb4 + 3] * inv_l)};
                     const int ch = (4 * dc + rb4) ^ (wrow & 7);
                     *reinterpret_cast<u32x2 *>(slot + wrow * RB + 16 * ch + 8 * half) = pr;
                 }
         };
-        pend_lse_v = l_run[0] > 0.f ? a.scale * m_ref[0] + logf(l_run[0]) : -INFINITY;
-        pend_out = a.out + ((int64_t)(q0 + iw[0]) * H + h) * D;
-        pend_lse = a.lse + (int64_t)(q0 + iw[0]) * H + h;
+        pend_lse_v = l_run > 0.f ? a.scale * m_ref + logf(l_run) : -INFINITY;
+        pend_out = a.out + ((int64_t)(q0 + iw) * H + h) * D;
+        pend_lse = a.lse + (int64_t)(q0 + iw) * H + h;
         pend_n = max(0, min(32, nrows - 32 * wave));
         if constexpr (DEFER) {
             to_slot(o_lds + wave * SLOT);
@@ -606,10 +571,10 @@ __global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q
     }
 }
 
-template <int D, int RPW>
+template <int D>
 static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStream_t stream)
 {
-    using T = VarlenTile<D, RPW>;
+    using T = VarlenTile<D>;
     if (a.block_q != T::BQ) return hipErrorInvalidValue;
     // paged keys: one 1 KiB load's keys must lie in one block
     if (a.block_table && (1 << a.bs_shift) * T::ROWB < 1024) return hipErrorInvalidValue;
@@ -617,11 +582,11 @@ static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStr
     const int64_t slots = (int64_t)num_cus * T::MIN_BLOCKS;
     const dim3 grid((unsigned)(a.n_items < slots ? a.n_items : slots)), block(T::THREADS);
     if (a.block_table) {
-        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, true, RPW>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, true, RPW>), grid, block, 0, stream, a);
+        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, true>), grid, block, 0, stream, a);
     } else {
-        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, false, RPW>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, false, RPW>), grid, block, 0, stream, a);
+        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, false>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -629,9 +594,9 @@ static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStr
 hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream)
 {
     switch (head_dim) {
-    case 64: return launch_d<64, 1>(a, causal, num_cus, stream);
-    case 128: return launch_d<128, 1>(a, causal, num_cus, stream);
-    case 256: return launch_d<256, 1>(a, causal, num_cus, stream);
+    case 64: return launch_d<64>(a, causal, num_cus, stream);
+    case 128: return launch_d<128>(a, causal, num_cus, stream);
+    case 256: return launch_d<256>(a, causal, num_cus, stream);
     default: return hipErrorInvalidValue;
     }
 }
