@@ -736,17 +736,25 @@ int oracle_paged_gather(const uint16_t *pool, const int32_t *block_table, const 
 /*                                                                          */
 /* Sequence b is cut into n_b = ceil(Lq_b / block_q) query tiles.  Tiles are */
 /* listed level by level: level r holds tile index qt = r of every sequence */
-/* with n_b > r, in ascending b; levels run from the highest r down to 0.   */
-/* Under causal masking with Lq == Lk a tile at level r sees r+1 key tiles, */
-/* so this lists the most expensive tiles first.  Each tile expands into    */
-/* num_heads items, head innermost: item = tile_position * H + h.           */
+/* with n_b > r; levels run from the highest r down to 0.  Under causal     */
+/* masking with Lq == Lk a tile at level r sees r+1 key tiles, so this      */
+/* lists the most expensive tiles first.  Inside a level the sequences come */
+/* in ascending b when sort_grain is 0; otherwise in descending order of    */
+/* ceil(Lq_b / sort_grain), ties in ascending b (the cost of a sequence's   */
+/* last tile, in key tiles of sort_grain keys, when Lq == Lk).  Each tile   */
+/* expands into num_heads items, head innermost: item = position * H + h.  */
+/* The order is a scheduling choice (the pages leave the mapping of tiles   */
+/* to thread blocks open); this is the list the GPU work decoder must       */
+/* reproduce exactly.                                                       */
 /* Output: items[3*w .. 3*w+2] = (b, qt, h).  Returns the item count, or    */
 /* -1 if capacity is too small or arguments are bad.                        */
 /* ------------------------------------------------------------------------ */
+static int64_t seq_len_at(const int32_t *cu_q, int32_t b) { return (int64_t)cu_q[b + 1] - cu_q[b]; }
+
 int64_t oracle_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_heads, int32_t block_q,
-                               int32_t *items, int64_t capacity)
+                               int32_t sort_grain, int32_t *items, int64_t capacity)
 {
-    if (batch < 0 || num_heads <= 0 || block_q <= 0) return -1;
+    if (batch < 0 || num_heads <= 0 || block_q <= 0 || sort_grain < 0) return -1;
     int64_t max_tiles = 0;
     for (int32_t b = 0; b < batch; b++) {
         const int64_t L = (int64_t)cu_q[b + 1] - cu_q[b];
@@ -754,14 +762,34 @@ int64_t oracle_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_h
         const int64_t n = (L + block_q - 1) / block_q;
         if (n > max_tiles) max_tiles = n;
     }
+    /* the order of the sequences inside every level: ascending b, then (with
+       a grain) a stable insertion sort by descending ceil(L / grain) */
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(batch > 0 ? batch : 1));
+    if (!order) return -1;
+    for (int32_t b = 0; b < batch; b++) order[b] = b;
+    if (sort_grain > 0) {
+        for (int32_t i = 1; i < batch; i++) {
+            const int32_t x = order[i];
+            const int64_t kx = (seq_len_at(cu_q, x) + sort_grain - 1) / sort_grain;
+            int32_t j = i;
+            while (j > 0 && (seq_len_at(cu_q, order[j - 1]) + sort_grain - 1) / sort_grain < kx) {
+                order[j] = order[j - 1];
+                j--;
+            }
+            order[j] = x;
+        }
+    }
     int64_t w = 0;
     for (int64_t r = max_tiles - 1; r >= 0; r--) {
-        for (int32_t b = 0; b < batch; b++) {
-            const int64_t L = (int64_t)cu_q[b + 1] - cu_q[b];
-            const int64_t n = (L + block_q - 1) / block_q;
+        for (int32_t i = 0; i < batch; i++) {
+            const int32_t b = order[i];
+            const int64_t n = (seq_len_at(cu_q, b) + block_q - 1) / block_q;
             if (n <= r) continue;
             for (int32_t h = 0; h < num_heads; h++) {
-                if (w >= capacity) return -1;
+                if (w >= capacity) {
+                    free(order);
+                    return -1;
+                }
                 items[3 * w + 0] = b;
                 items[3 * w + 1] = (int32_t)r;
                 items[3 * w + 2] = h;
@@ -769,5 +797,6 @@ int64_t oracle_varlen_tile_map(const int32_t *cu_q, int32_t batch, int32_t num_h
             }
         }
     }
+    free(order);
     return w;
 }

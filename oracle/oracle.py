@@ -62,7 +62,7 @@ def _bind(lib):
     lib.oracle_paged_decode_finalize.restype = ctypes.c_int
     lib.oracle_paged_gather.argtypes = [u16p, i32p, i32p, i32, i32, i32, i32, i32, u16p]
     lib.oracle_paged_gather.restype = ctypes.c_int
-    lib.oracle_varlen_tile_map.argtypes = [i32p, i32, i32, i32, i32p, i64]
+    lib.oracle_varlen_tile_map.argtypes = [i32p, i32, i32, i32, i32, i32p, i64]
     lib.oracle_varlen_tile_map.restype = ctypes.c_int64
     return lib
 
@@ -271,9 +271,11 @@ def paged_gather(pool, block_table, context_lens, fill=0xFFFF, lib=None):
     return dense
 
 
-def varlen_tile_map(cu_q, num_heads, block_q, lib=None):
+def varlen_tile_map(cu_q, num_heads, block_q, sort_grain=0, lib=None):
     """Canonical work list of the tiled forward pass: int32 [n_items, 3] of
-    (sequence, query tile, head), most expensive tile level first."""
+    (sequence, query tile, head), most expensive tile level first; inside a
+    level, sequences in ascending b (sort_grain 0) or in descending
+    ceil(L / sort_grain), ties in ascending b."""
     lib = lib or load()
     cu_q = _c(cu_q, np.int32)
     B = len(cu_q) - 1
@@ -282,7 +284,7 @@ def varlen_tile_map(cu_q, num_heads, block_q, lib=None):
         cap += -(-(int(cu_q[b + 1]) - int(cu_q[b])) // block_q)
     cap = max(cap * num_heads, 1)
     items = np.zeros((cap, 3), dtype=np.int32)
-    n = lib.oracle_varlen_tile_map(cu_q, B, num_heads, block_q, items, cap)
+    n = lib.oracle_varlen_tile_map(cu_q, B, num_heads, block_q, int(sort_grain), items, cap)
     if n < 0:
         raise ValueError("oracle_varlen_tile_map rejected its arguments")
     return items[:n]

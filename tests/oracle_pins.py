@@ -628,30 +628,38 @@ def pin_decode_gather(lib):
 
 # --- tile-map pins --------------------------------------------------------------------
 
-def brute_force_tile_map(cu_q, H, BQ):
-    """All (b, qt, h) with qt < ceil(L_b / BQ), sorted by qt descending, then b,
-    then h."""
+def brute_force_tile_map(cu_q, H, BQ, grain=0):
+    """All (b, qt, h) with qt < ceil(L_b / BQ), sorted by qt descending, then
+    (with a grain) ceil(L_b / grain) descending, then b, then h."""
     items = []
     for b in range(len(cu_q) - 1):
-        n = -(-(int(cu_q[b + 1]) - int(cu_q[b])) // BQ)
+        L = int(cu_q[b + 1]) - int(cu_q[b])
+        n = -(-L // BQ)
+        key = -(-L // grain) if grain else 0
         for qt in range(n):
             for h in range(H):
-                items.append((b, qt, h))
-    items.sort(key=lambda x: (-x[1], x[0], x[2]))
-    return np.array(items, np.int32).reshape(-1, 3)
+                items.append((-qt, -key, b, h))
+    items.sort()
+    return np.array([(b, -nqt, h) for nqt, _, b, h in items], np.int32).reshape(-1, 3)
 
 
 def pin_tile_map(lib):
     rng = np.random.Generator(np.random.PCG64(26))
-    for trial in range(20):
+    for trial in range(40):
         B = int(rng.integers(0, 20))
         L = rng.integers(0, 700, size=B)
         cu = cu_from_lengths(L)
         H = int(rng.integers(1, 5))
         BQ = int(rng.choice([16, 64, 128]))
-        got = O.varlen_tile_map(cu, H, BQ, lib=lib)
-        ref = brute_force_tile_map(cu, H, BQ)
-        assert np.array_equal(got, ref), (trial, B, H, BQ)
+        grain = int(rng.choice([0, BQ // 4, BQ // 2, BQ]))
+        got = O.varlen_tile_map(cu, H, BQ, grain, lib=lib)
+        ref = brute_force_tile_map(cu, H, BQ, grain)
+        assert np.array_equal(got, ref), (trial, B, H, BQ, grain)
+    # a hand-checked case: lengths 5, 130, 64, 200 with BQ = 128, grain 64:
+    # level 1 holds tiles of b = 1 (key 3) and b = 3 (key 4): b = 3 first;
+    # level 0: keys 1, 3, 1, 4 -> b = 3, 1, 0, 2
+    got = O.varlen_tile_map(cu_from_lengths([5, 130, 64, 200]), 1, 128, 64, lib=lib)
+    assert got.tolist() == [[3, 1, 0], [1, 1, 0], [3, 0, 0], [1, 0, 0], [0, 0, 0], [2, 0, 0]]
 
 
 ALL_PINS = [

@@ -13,6 +13,24 @@ from variable_length_flashattention_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 
+SCHED_INTS = 3584  # LDS ints of the kernels' work-list tables
+SORT_SCRATCH = 256
+SORT_MIN_BATCH = 64
+
+
+def device_sort_grain(B, maxq, bq, D):
+    """The grain by which the forward's work list orders sequences inside a
+    level (0: ascending b): its key tile, for batches of at least 64
+    sequences whose tables fit in LDS with the permutation and have at most
+    64 distinct sort keys."""
+    grain = 64 if D <= 128 else 32
+    levels = -(-maxq // bq)
+    cached = 2 * (B + 1) + 2 * (levels + 1) <= SCHED_INTS
+    keys = levels * (bq // grain)
+    fits = 3 * (B + 1) + 2 * (levels + 1) + SORT_SCRATCH <= SCHED_INTS
+    return grain if cached and B >= SORT_MIN_BATCH and 1 <= keys <= 64 and fits else 0
+
+
 def device_tile_map(cu, H, D):
     B = len(cu) - 1
     maxq = int(np.max(np.diff(cu))) if B else 0
@@ -21,29 +39,36 @@ def device_tile_map(cu, H, D):
     items = torch.full((cap * 3,), -7, dtype=torch.int32, device="cuda")
     say(f"  launch rra_debug_varlen_tile_map B={B} H={H} D={D} maxq={maxq}")
     n = rra.rra_debug_varlen_tile_map(dev_i32(cu), B, H, maxq, D, items, cap)
-    return items.cpu().numpy().reshape(-1, 3)[:n], bq
+    return items.cpu().numpy().reshape(-1, 3)[:n], bq, device_sort_grain(B, maxq, bq, D)
 
 
-@pytest.mark.parametrize("seed,B,maxlen,H,D", [
-    (1, 16, 2048, 32, 128), (2, 4, 9000, 16, 128), (3, 1024, 128, 8, 64), (4, 100, 700, 3, 256),
-    (5, 9500, 40, 1, 128),  # more sequences than the kernel caches in LDS
-    (6, 7, 1, 5, 64),
+@pytest.mark.parametrize("seed,B,maxlen,H,D,sorted_", [
+    (1, 16, 2048, 32, 128, False), (2, 4, 9000, 16, 128, False), (3, 1024, 128, 8, 64, True),
+    (4, 100, 700, 3, 256, True),
+    (5, 9500, 40, 1, 128, False),   # more sequences than the kernel caches in LDS
+    (6, 7, 1, 5, 64, False),
+    (7, 1200, 100, 2, 64, False),   # cached, but no room for the permutation
+    (8, 140, 2100, 2, 256, False),  # cached, more than 64 sort keys
+    (9, 600, 300, 3, 256, True),    # keys 1..12 across ten 64-sequence chunks
+    (10, 64, 500, 2, 128, True),    # the smallest sorted batch
+    (11, 63, 500, 2, 128, False),
 ])
-def test_tile_map_bit_exact(seed, B, maxlen, H, D):
+def test_tile_map_bit_exact(seed, B, maxlen, H, D, sorted_):
     rng = np.random.Generator(np.random.PCG64(seed))
     L = rng.integers(0, maxlen + 1, size=B)
     cu = I.cu_from_lengths(L)
-    got, bq = device_tile_map(cu, H, D)
-    ref = O.varlen_tile_map(cu, H, bq)
+    got, bq, grain = device_tile_map(cu, H, D)
+    assert (grain > 0) == sorted_
+    ref = O.varlen_tile_map(cu, H, bq, grain)
     n = len(ref)
     assert np.array_equal(got[:n], ref)
     assert np.all(got[n:] == -1)
 
 
 def test_tile_map_configs():
-    for c in (I.tiny(True), I.mixed(), I.skewed(), I.many_short(64, True)):
-        got, bq = device_tile_map(c.cu_q, c.num_heads, c.head_dim)
-        ref = O.varlen_tile_map(c.cu_q, c.num_heads, bq)
+    for c in (I.tiny(True), I.mixed(), I.skewed(), I.many_short(64, True), I.many_short(256, True)):
+        got, bq, grain = device_tile_map(c.cu_q, c.num_heads, c.head_dim)
+        ref = O.varlen_tile_map(c.cu_q, c.num_heads, bq, grain)
         assert np.array_equal(got[:len(ref)], ref) and np.all(got[len(ref):] == -1), c.name
 
 

@@ -64,8 +64,9 @@ MUTANTS = [
      "rowdot = 0.0;\n                for (int64_t d = 0; d < D; d++) rowdot += bf16_value(dorow[d]) * orow[d];",
      "(void)orow;"),
     ("tile_levels_ascending", "for (int64_t r = max_tiles - 1; r >= 0; r--) {", "for (int64_t r = 0; r < max_tiles; r++) {"),
-    ("tile_count_floor", "const int64_t n = (L + block_q - 1) / block_q;\n            if (n <= r) continue;",
-     "const int64_t n = L / block_q;\n            if (n <= r) continue;"),
+    ("tile_count_floor", "const int64_t n = (seq_len_at(cu_q, b) + block_q - 1) / block_q;",
+     "const int64_t n = seq_len_at(cu_q, b) / block_q;"),
+    ("tile_sort_ascending", "+ sort_grain - 1) / sort_grain < kx) {", "+ sort_grain - 1) / sort_grain > kx) {"),
 ]
 
 

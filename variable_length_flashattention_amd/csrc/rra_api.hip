@@ -350,8 +350,9 @@ int32_t rra_debug_varlen_tile_map(const int32_t *cu_seqlens_q, int32_t batch, in
     if (n == 0) return RRA_OK;
     if (!cu_seqlens_q || !items_out || capacity < n) return RRA_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_varlen_tile_map(cu_seqlens_q, cu_seqlens_q, batch, num_heads, bq, (int32_t)tiles_per_seq, n,
-                                          items_out, st);
+    hipError_t e = launch_varlen_tile_map(cu_seqlens_q, cu_seqlens_q, batch, num_heads, bq,
+                                          varlen_sort_grain(head_dim, batch, (int32_t)tiles_per_seq),
+                                          (int32_t)tiles_per_seq, n, items_out, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     return hip_status(e);
 }

@@ -16,6 +16,9 @@ inline int varlen_block_q(int head_dim, int max_seqlen_q)
     (void)max_seqlen_q;
     return 128;
 }
+// Keys per key tile of the forward kernel (64, or 32 at head_dim 256): also
+// the cost grain by which its work list orders the sequences of a level.
+constexpr int varlen_block_k(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 // LDS ints a forward workgroup sets aside for its work-list tables (enough
 // for about 1700 sequences; more fall back to decoding from global memory).
 constexpr int kSchedInts = 3584;
@@ -61,8 +64,11 @@ constexpr int kBwdKRows = 128;  // keys per dk/dv work item
 hipError_t launch_varlen_bwd(const BwdArgs &a, bool causal, int num_cus, hipStream_t stream);
 
 hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream);
+// The cost grain by which the forward kernel orders the sequences of a level
+// for this batch (0: ascending b), and so the grain its tile map uses.
+int32_t varlen_sort_grain(int32_t head_dim, int32_t batch, int32_t levels);
 hipError_t launch_varlen_tile_map(const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
-                                  int32_t block_q, int32_t levels, int64_t n_items, int32_t *items_out,
+                                  int32_t block_q, int32_t grain, int32_t levels, int64_t n_items, int32_t *items_out,
                                   hipStream_t stream);
 
 // Where a sequence's token count comes from: context_lens[s] when given;

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void varlen_bwd_dq_kernel(
     const int H = a.num_heads, Hkv = a.num_kv_heads;
     const float sl2 = a.scale_log2;
     float *ws_lse2 = a.ws, *ws_dsum = a.ws + (int64_t)H * a.total_q;
-    const WorkTables wt = build_work_tables(a.cu_q, a.cu_k, a.batch + 1, a.batch, BQ, a.levels_q, sched, kSchedInts);
+    const WorkTables wt = build_work_tables(a.cu_q, a.cu_k, a.batch + 1, a.batch, BQ, 0, a.levels_q, sched, kSchedInts);
 
     for (int64_t k = 0;; k++) {
         const int64_t w = serpentine_item(k, blockIdx.x, gridDim.x);
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void varlen_bwd_dkv_kernel(
     const int H = a.num_heads, Hkv = a.num_kv_heads, R = a.gqa_ratio;
     const float sl2 = a.scale_log2;
     // (the key offsets are the tiled list here, the query offsets the other)
-    const WorkTables wt = build_work_tables(a.cu_k, a.cu_q, a.batch + 1, a.batch, BKB, a.levels_k, sched, kSchedInts);
+    const WorkTables wt = build_work_tables(a.cu_k, a.cu_q, a.batch + 1, a.batch, BKB, 0, a.levels_k, sched, kSchedInts);
     const __amdgpu_buffer_rsrc_t ws_r = raw_buffer(a.ws);
 
     for (int64_t k = 0;; k++) {

@@ -43,7 +43,7 @@ template <int D>
 struct VarlenTile {
     static constexpr int NW = 4;                       // waves per workgroup
     static constexpr int BQ = 32 * NW;                 // query rows per work item (32 per wave)
-    static constexpr int BK = D <= 128 ? 64 : 32;
+    static constexpr int BK = varlen_block_k(D);
     static constexpr int NBUF = 2;                     // K/V tile buffers (one in flight, one in use)
     static constexpr int ROWB = D * 2;                 // bytes per K/V row
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -61,7 +61,9 @@ struct VarlenTile {
     static constexpr int MIN_BLOCKS = D == 64 ? 3 : D == 128 ? 2 : 1;
 };
 
-template <int D, bool CAUSAL, bool PAGED>
+// SORTED: the work list orders the sequences of a level by length (the
+// work-list tables sort them at the kernel's start).
+template <int D, bool CAUSAL, bool PAGED, bool SORTED>
 __global__ __launch_bounds__((VarlenTile<D>::THREADS), (VarlenTile<D>::MIN_BLOCKS)) void varlen_fwd_kernel(VarlenArgs a)
 {
     using T = VarlenTile<D>;
@@ -86,8 +88,8 @@ __global__ __launch_bounds__((VarlenTile<D>::THREADS), (VarlenTile<D>::MIN_BLOCK
     const int H = a.num_heads;
     const float sl2 = a.scale_log2;
     const int32_t *kcount = PAGED ? a.seqlens_k : a.cu_k;  // per-sequence key counts, or key offsets
-    const WorkTables wt = build_work_tables(a.cu_q, kcount, PAGED ? a.batch : a.batch + 1, a.batch, BQ, a.levels,
-                                            sched, kSchedInts);
+    const WorkTables wt = build_work_tables(a.cu_q, kcount, PAGED ? a.batch : a.batch + 1, a.batch, BQ,
+                                            SORTED ? BK : 0, a.levels, sched, kSchedInts);
 
     // Output stores.  The accumulators hold O^T, 4 consecutive d of one query
     // per register quad, so stores straight from them would write 8-byte
@@ -553,12 +555,12 @@ __global__ __launch_bounds__((VarlenTile<D>::THREADS), (VarlenTile<D>::MIN_BLOCK
 
 // Test hook: the same work tables and decoder, one wave per workgroup.
 __global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q, const int32_t *cu_k, int32_t batch,
-                                                             int32_t num_heads, int32_t block_q, int32_t levels,
-                                                             int64_t n_items, int32_t *items)
+                                                             int32_t num_heads, int32_t block_q, int32_t grain,
+                                                             int32_t levels, int64_t n_items, int32_t *items)
 {
     __shared__ int sched[kSchedInts];
     const int lane = threadIdx.x;
-    const WorkTables wt = build_work_tables(cu_q, cu_k, batch + 1, batch, block_q, levels, sched, kSchedInts);
+    const WorkTables wt = build_work_tables(cu_q, cu_k, batch + 1, batch, block_q, grain, levels, sched, kSchedInts);
     for (int64_t w = blockIdx.x; w < n_items; w += gridDim.x) {
         int b = -1, qt = -1, h = -1;
         const bool ok = decode_work_item(wt, cu_q, num_heads, w, lane, b, qt, h);
@@ -571,6 +573,13 @@ __global__ __launch_bounds__(64) void varlen_tile_map_kernel(const int32_t *cu_q
     }
 }
 
+template <int D, bool CAUSAL, bool PAGED>
+static void launch_fwd(bool sorted, dim3 grid, dim3 block, hipStream_t stream, const VarlenArgs &a)
+{
+    if (sorted) hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL, PAGED, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL, PAGED, false>), grid, block, 0, stream, a);
+}
+
 template <int D>
 static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStream_t stream)
 {
@@ -581,14 +590,23 @@ static hipError_t launch_d(const VarlenArgs &a, bool causal, int num_cus, hipStr
     // persistent grid: as many workgroups as fit on the device at once
     const int64_t slots = (int64_t)num_cus * T::MIN_BLOCKS;
     const dim3 grid((unsigned)(a.n_items < slots ? a.n_items : slots)), block(T::THREADS);
+    const bool sorted = varlen_sort_grain(D, a.batch, a.levels) > 0;
     if (a.block_table) {
-        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, true>), grid, block, 0, stream, a);
+        if (causal) launch_fwd<D, true, true>(sorted, grid, block, stream, a);
+        else launch_fwd<D, false, true>(sorted, grid, block, stream, a);
     } else {
-        if (causal) hipLaunchKernelGGL((varlen_fwd_kernel<D, true, false>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((varlen_fwd_kernel<D, false, false>), grid, block, 0, stream, a);
+        if (causal) launch_fwd<D, true, false>(sorted, grid, block, stream, a);
+        else launch_fwd<D, false, false>(sorted, grid, block, stream, a);
     }
     return hipGetLastError();
+}
+
+int32_t varlen_sort_grain(int32_t head_dim, int32_t batch, int32_t levels)
+{
+    const int g = varlen_block_k(head_dim);
+    const bool sort = batch >= kSortMinBatch &&
+                      work_tables_sorted(batch, levels, varlen_block_q(head_dim, 0), g, kSchedInts);
+    return sort ? g : 0;
 }
 
 hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int num_cus, hipStream_t stream)
@@ -602,12 +620,12 @@ hipError_t launch_varlen_fwd(const VarlenArgs &a, int head_dim, bool causal, int
 }
 
 hipError_t launch_varlen_tile_map(const int32_t *cu_q, const int32_t *cu_k, int32_t batch, int32_t num_heads,
-                                  int32_t block_q, int32_t levels, int64_t n_items, int32_t *items_out,
+                                  int32_t block_q, int32_t grain, int32_t levels, int64_t n_items, int32_t *items_out,
                                   hipStream_t stream)
 {
     const unsigned grid = (unsigned)(n_items < 1024 ? n_items : 1024);
     hipLaunchKernelGGL(varlen_tile_map_kernel, dim3(grid), dim3(64), 0, stream, cu_q, cu_k, batch, num_heads, block_q,
-                       levels, n_items, items_out);
+                       grain, levels, n_items, items_out);
     return hipGetLastError();
 }
 
