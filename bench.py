@@ -370,7 +370,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic("varlen_fwd_mixed", kernel_source_hash(VARLEN_SOURCES)),
-                     "kernel": "varlen_fwd_kernel<128,true>", "avg_launch_us": round(avg_launch * 1e6, 2),
+                     "kernel": "varlen_fwd_kernel<128, true, false, false>", "avg_launch_us": round(avg_launch * 1e6, 2),
                      "algorithmic_bytes": I.varlen_bytes(mixed)},
     }
 
