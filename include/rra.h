@@ -327,7 +327,12 @@ int32_t rra_unpack_rows(const void *packed, void *padded, const int32_t *cu_seql
  * rra_debug_varlen_tile_map: runs the forward kernel's own work-item decoder
  * for every launched work item and writes items_out[3*w..3*w+2] =
  * (sequence, query tile, head) of item w, or (-1,-1,-1) for launched items
- * beyond the last one.  *item_count receives the number of launched items
+ * beyond the last one.  The order is the one the forward kernel uses for the
+ * same batch and head_dim: levels from the highest query tile down, and
+ * inside a level the sequences in ascending index, or, for batches of at
+ * least 64 sequences whose work tables can hold the permutation and that
+ * have at most 64 distinct keys ceil(Lq / key tile), in descending key with
+ * ties in ascending index.  *item_count receives the number of launched items
  * (host value).  items_out must hold 3 * capacity int32; capacity must be at
  * least the launched count, which is batch * ceil(max_seqlen_q / block_q) *
  * num_heads with block_q = rra_varlen_block_q(head_dim, max_seqlen_q).
