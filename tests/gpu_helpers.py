@@ -69,3 +69,21 @@ def compare(out, lse, ref_out, ref_lse, what):
     assert eo <= OUT_TOL, f"{what}: max|dout| {eo}"
     assert el <= LSE_TOL, f"{what}: max|dlse| {el}"
     return eo, el
+
+
+SCHED_INTS = 3584  # LDS ints of the kernels' work-list tables
+SORT_SCRATCH = 256
+SORT_MIN_BATCH = 64
+
+
+def device_sort_grain(B, maxq, bq, D):
+    """The grain by which the forward's work list orders sequences inside a
+    level (0: ascending b): its key tile, for batches of at least 64
+    sequences whose tables fit in LDS with the permutation and have at most
+    64 distinct sort keys."""
+    grain = 64 if D <= 128 else 32
+    levels = -(-maxq // bq)
+    cached = 2 * (B + 1) + 2 * (levels + 1) <= SCHED_INTS
+    keys = levels * (bq // grain)
+    fits = 3 * (B + 1) + 2 * (levels + 1) + SORT_SCRATCH <= SCHED_INTS
+    return grain if cached and B >= SORT_MIN_BATCH and 1 <= keys <= 64 and fits else 0

@@ -7,28 +7,10 @@ import torch
 
 import oracle as O
 import variable_length_flashattention_amd as rra
-from gpu_helpers import dev_bf16, dev_i32, say
+from gpu_helpers import dev_bf16, dev_i32, say, device_sort_grain
 from variable_length_flashattention_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
-
-
-SCHED_INTS = 3584  # LDS ints of the kernels' work-list tables
-SORT_SCRATCH = 256
-SORT_MIN_BATCH = 64
-
-
-def device_sort_grain(B, maxq, bq, D):
-    """The grain by which the forward's work list orders sequences inside a
-    level (0: ascending b): its key tile, for batches of at least 64
-    sequences whose tables fit in LDS with the permutation and have at most
-    64 distinct sort keys."""
-    grain = 64 if D <= 128 else 32
-    levels = -(-maxq // bq)
-    cached = 2 * (B + 1) + 2 * (levels + 1) <= SCHED_INTS
-    keys = levels * (bq // grain)
-    fits = 3 * (B + 1) + 2 * (levels + 1) + SORT_SCRATCH <= SCHED_INTS
-    return grain if cached and B >= SORT_MIN_BATCH and 1 <= keys <= 64 and fits else 0
 
 
 def device_tile_map(cu, H, D):

@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import variable_length_flashattention_amd as rra
-from gpu_helpers import OUT_TOL, compare, dev_bf16, dev_i32, host_f64, run_varlen, say
+from gpu_helpers import OUT_TOL, compare, dev_bf16, dev_i32, device_sort_grain, host_f64, run_varlen, say
 from variable_length_flashattention_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -51,6 +51,53 @@ def test_paged_forward_random(seed):
     torch.cuda.synchronize()
     ro, rl = O.varlen_attn_paged(c.q, c.k_pool, c.v_pool, c.cu_q, c.seqlens_k, c.block_table, c.scale, causal)
     compare(host_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"random paged forward {seed}")
+
+
+def draw_many(seed):
+    """Batches of 64-400 sequences (the forward kernel's length-sorted work
+    list): lengths U[0,300] with empty sequences, k lengths equal to q or
+    drawn apart (some 0), 1-2 kv heads."""
+    rng = np.random.Generator(np.random.PCG64(9500 + seed))
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2]))
+    H = Hkv * int(rng.choice([1, 2]))
+    B = int(rng.integers(64, 401))
+    lq = rng.integers(0, 301, size=B)
+    lq[rng.random(B) < 0.05] = 0
+    lk = np.where(rng.random(B) < 0.7, lq, rng.integers(0, 400, size=B))
+    causal = bool(rng.integers(0, 2))
+    return rng, D, H, Hkv, lq, lk, causal
+
+
+MANY_SEEDS = list(range(8))
+
+
+@pytest.mark.parametrize("seed", MANY_SEEDS)
+def test_forward_random_sorted(seed):
+    rng, D, H, Hkv, lq, lk, causal = draw_many(seed)
+    assert device_sort_grain(len(lq), int(lq.max()), 128, D) > 0  # the sorted kernel runs
+    c = I.varlen_case(f"many{seed}", lq, lk, H, D, seed=seed, causal=causal, num_kv_heads=Hkv)
+    out, lse = run_varlen(c)
+    ro, rl = O.varlen_attn(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+    compare(out, lse, ro, rl, f"random forward, sorted work list {seed}")
+
+
+@pytest.mark.parametrize("seed", MANY_SEEDS[:4])
+def test_paged_forward_random_sorted(seed):
+    rng, D, H, Hkv, lq, lk, causal = draw_many(seed)
+    assert device_sort_grain(len(lq), int(lq.max()), 128, D) > 0
+    BS = int(rng.choice([8, 16, 64]))
+    c = I.paged_prefill_case(f"pmany{seed}", lq, lk, H, D, BS, seed=seed, causal=causal, num_kv_heads=Hkv,
+                             spare_blocks=2)
+    q = dev_bf16(c.q)
+    say(f"  launch rra_varlen_attn_fwd_paged (sorted) seed={seed} B={c.batch} H={H} Hkv={Hkv} D={D} BS={BS} "
+        f"causal={causal}")
+    out, lse = rra.varlen_attn_fwd_paged(q, dev_bf16(c.k_pool), dev_bf16(c.v_pool), dev_i32(c.cu_q),
+                                         dev_i32(c.seqlens_k), dev_i32(c.block_table), c.max_seqlen_q, c.scale,
+                                         causal)
+    torch.cuda.synchronize()
+    ro, rl = O.varlen_attn_paged(c.q, c.k_pool, c.v_pool, c.cu_q, c.seqlens_k, c.block_table, c.scale, causal)
+    compare(host_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"random paged forward, sorted {seed}")
 
 
 @pytest.mark.parametrize("seed", SEEDS)
