@@ -226,6 +226,22 @@ __global__ __launch_bounds__((VarlenTile<D>::THREADS), (VarlenTile<D>::MIN_BLOCK
         for (int j = 0; j < NKO; j++)
             plane_k[j] = (uint32_t)(lrow * row_bytes + 16 * (pch ^ T::swz_k(srow0 + j * RPL)));
         const uint32_t plane_v = (uint32_t)(lrow * row_bytes + 16 * (pch ^ T::swz_v(srow0)));
+        // paged, blocks of at least KPW keys: wave w stages the tile's pieces
+        // w*WL .. w*WL+WL-1 instead, i.e. keys KPW*w .. KPW*w+KPW-1, which lie in
+        // one pool block: one table entry and one descriptor per tile, and per
+        // piece a per-lane offset holding the key's row past the wave's first
+        // key and the swizzled chunk
+        constexpr int KPW = WL * RPB;
+        const bool one_block = PAGED && (1 << a.bs_shift) >= KPW;
+        uint32_t wk[PAGED ? WL : 1], wv[PAGED ? WL : 1];
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int i = 0; i < WL; i++) {
+                const int lr = i * RPB + lrow, trow = wave * KPW + lr;
+                wk[i] = (uint32_t)(lr * row_bytes + 16 * (pch ^ T::swz_k(trow)));
+                wv[i] = (uint32_t)(lr * row_bytes + 16 * (pch ^ T::swz_v(trow)));
+            }
+        }
         const int32_t *table = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
         const int last_blk = PAGED ? (Lk - 1) >> a.bs_shift : 0;
         // lane j holds the table entry of block (tile's first block + j),
@@ -240,6 +256,23 @@ __global__ __launch_bounds__((VarlenTile<D>::THREADS), (VarlenTile<D>::MIN_BLOCK
             const int blk0 = kbase >> a.bs_shift;
             const int cur = tab;
             if (kt + 1 < nkt) tab = fetch_table(kt + 1);  // the next tile's, a tile ahead
+            if (one_block) {
+                const int r0 = min(kbase + wave * KPW, Lk - 1);  // the wave's first key (the last key past the end)
+                const int ent = __builtin_amdgcn_readlane(cur, (r0 >> a.bs_shift) - blk0);
+                const int64_t prow = ((int64_t)ent << a.bs_shift) + (r0 & ((1 << a.bs_shift) - 1));
+                const int64_t off = (prow * a.num_kv_heads + kh) * ROWB;
+                const __amdgpu_buffer_rsrc_t kr = raw_buffer(reinterpret_cast<const uint8_t *>(a.k) + off);
+                const __amdgpu_buffer_rsrc_t vr = raw_buffer(reinterpret_cast<const uint8_t *>(a.v) + off);
+                const int lim = Lk - 1 - r0;  // keys past r0 + lim re-read key r0 + lim
+#pragma unroll
+                for (int i = 0; i < WL; i++) {
+                    const int lr = i * RPB + lrow;
+                    const uint32_t back = lr > lim ? (uint32_t)((lr - lim) * row_bytes) : 0u;
+                    buffer_to_lds16(kr, kb + (wave * WL + i) * 1024, wk[i] - back, 0);
+                    buffer_to_lds16(vr, vb + (wave * WL + i) * 1024, wv[i] - back, 0);
+                }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < WL; i++) {
                 const int piece = i * NW + wave;
