@@ -518,23 +518,22 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 }
 
 // finalize of the stateful interface: out = o / l, 0 where l == 0.  One
-// wave per (sequence, q head).
+// thread per 4 floats of o; its o and its unit's l are loaded together.
 __global__ __launch_bounds__(256) void decode_finalize_kernel(const float *state_l, const float *state_o,
                                                               uint16_t *out, int64_t units, int32_t D)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (u >= units) return;
-    const float l = state_l[u];
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units * (D / 4)) return;
+    const f32x4 o = reinterpret_cast<const f32x4 *>(state_o)[i];
+    const float l = state_l[i / (D / 4)];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    for (int d = 4 * lane; d < D; d += 256) {
-        const f32x4 o = *reinterpret_cast<const f32x4 *>(state_o + u * D + d);
-        const u32x2 pr = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
-        *reinterpret_cast<u32x2 *>(out + u * D + d) = pr;
-    }
+    const u32x2 pr = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+    reinterpret_cast<u32x2 *>(out)[i] = pr;
 }
 
-// The stateful interface's initial state: m = -inf, l = 0, o = 0.
+// The stateful interface's initial state: m = -inf, l = 0, o = 0.  One
+// thread per unit for m and l and per 4 floats of o (16-byte stores; D is a
+// multiple of 4 and o 16-byte aligned).
 __global__ __launch_bounds__(256) void decode_state_init_kernel(float *state_m, float *state_l, float *state_o,
                                                                 int64_t units, int32_t D)
 {
@@ -543,16 +542,16 @@ __global__ __launch_bounds__(256) void decode_state_init_kernel(float *state_m, 
         state_m[i] = -INFINITY;
         state_l[i] = 0.f;
     }
-    const int64_t n = units * D;
-    for (int64_t j = i; j < n; j += (int64_t)gridDim.x * 256) state_o[j] = 0.f;
+    if (i < units * (D / 4)) reinterpret_cast<f32x4 *>(state_o)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 hipError_t launch_decode_finalize(const float *state_l, const float *state_o, uint16_t *out, int64_t units,
                                   int32_t head_dim, hipStream_t stream)
 {
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_finalize_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, state_l,
-                       state_o, out, units, head_dim);
+    const int64_t blocks = (units * (head_dim / 4) + 255) / 256;
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, state_l, state_o, out,
+                       units, head_dim);
     return hipGetLastError();
 }
 
@@ -560,7 +559,8 @@ hipError_t launch_decode_state_init(float *state_m, float *state_l, float *state
                                     hipStream_t stream)
 {
     if (units == 0) return hipSuccess;
-    const int64_t blocks = (units + 255) / 256;
+    const int64_t threads = units * (head_dim / 4) > units ? units * (head_dim / 4) : units;
+    const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(decode_state_init_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, state_m, state_l,
                        state_o, units, head_dim);
     return hipGetLastError();

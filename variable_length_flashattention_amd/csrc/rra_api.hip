@@ -502,7 +502,7 @@ int32_t rra_paged_decode_state_init(float *state_m, float *state_l, float *state
     if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return RRA_ERR_INVALID_ARG;
     if (!supported_head_dim(head_dim)) return RRA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return RRA_OK;
-    if (!state_m || !state_l || !state_o) return RRA_ERR_INVALID_ARG;
+    if (!state_m || !state_l || !state_o || !aligned16(state_o)) return RRA_ERR_INVALID_ARG;
     return hip_status(launch_decode_state_init(state_m, state_l, state_o, (int64_t)num_seqs * num_q_heads,
                                                head_dim, static_cast<hipStream_t>(stream)));
 }
